@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for grouped-query attention over a KV cache.
+
+This module is shared by the tests, the bench and the smoke check. It draws
+random numbers and fixes storage formats; it contains none of the attention
+arithmetic (no scores, no softmax, no head mapping), so both the float64
+oracle and the GPU path can consume its arrays without sharing method code.
+
+Workloads (the five shapes the library is measured and checked on):
+
+  c1  tiny decode, fp32: B=1, Hq=8, Hkv=2, d=64, 256 cached tokens
+  c2  Llama-3-8B-shaped decode, bf16: B=32, Hq=32, Hkv=8, d=128, 8192 tokens
+  c3  wide-group decode, bf16: B=64, Hq=32, Hkv=2, d=128, ragged lengths
+      drawn uniformly from [1024, 32768] (inclusive), cache capacity 32768
+  c4  MQA long-context decode, bf16: B=4, Hq=16, Hkv=1, d=128, 131072 tokens
+  c5  causal prefill, bf16: B=2, Hq=32, Hkv=8, d=128, N=4096
+
+Recipe: seed = 1000 + workload index; ``SeedSequence(seed).spawn(4)`` gives
+independent PCG64 streams for (lengths, Q, K, V) in that order; values are
+i.i.d. standard normal drawn as float32 and, for bf16 workloads, rounded to
+bfloat16 with round-to-nearest-even.  Cache slots past a sequence's length
+are filled with NaN so that any kernel reading them is caught.
+
+Head-major layouts: q ``[B, Hq, d]`` (decode) or ``[B, Hq, N, d]`` (prefill);
+k/v ``[B, Hkv, T_cap, d]`` (decode cache) or ``[B, Hkv, N, d]`` (prefill).
+bf16 tensors are held as ``uint16`` bit patterns; ``bf16_bits_to_f32``
+widens them exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    dtype: str            # "f32" or "bf16": storage type of q, k, v
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    max_seq_len: int      # cache capacity T_cap
+    min_len: int          # lengths uniform in [min_len, max_len]
+    max_len: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def ragged(self) -> bool:
+        return self.min_len != self.max_len
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    seq_len: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+CONFIGS = {
+    "c1": DecodeConfig("tiny-decode-fp32", "f32", 1, 8, 2, 64, 256, 256, 256, 1001),
+    "c2": DecodeConfig("llama3-8b-decode-bf16", "bf16", 32, 32, 8, 128, 8192, 8192, 8192, 1002),
+    "c3": DecodeConfig("wide-group-ragged-decode-bf16", "bf16", 64, 32, 2, 128, 32768, 1024, 32768, 1003),
+    "c4": DecodeConfig("mqa-long-decode-bf16", "bf16", 4, 16, 1, 128, 131072, 131072, 131072, 1004),
+    "c5": PrefillConfig("causal-prefill-bf16", "bf16", 2, 32, 8, 128, 4096, 1005),
+}
+
+
+def describe(cfg) -> str:
+    """One-line workload description used in bench output and test ids."""
+    if isinstance(cfg, DecodeConfig):
+        lens = (f"T={cfg.max_len}" if not cfg.ragged
+                else f"T~U[{cfg.min_len},{cfg.max_len}] cap={cfg.max_seq_len}")
+        return (f"decode {cfg.dtype} B={cfg.batch} Hq={cfg.num_q_heads} "
+                f"Hkv={cfg.num_kv_heads} d={cfg.head_dim} {lens}")
+    return (f"causal prefill {cfg.dtype} B={cfg.batch} Hq={cfg.num_q_heads} "
+            f"Hkv={cfg.num_kv_heads} d={cfg.head_dim} N={cfg.seq_len}")
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 storage helpers (IEEE bit manipulation only)
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits.
+
+    Inputs must be finite (the generator only rounds normal draws)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of stored values (fp32 arrays or bf16 bit arrays)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _normals(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _streams(seed: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(4)]
+
+
+# ---------------------------------------------------------------------------
+# Generators
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DecodeInputs:
+    cfg: DecodeConfig
+    q: np.ndarray          # [B, Hq, d]          (float32 or uint16 bf16 bits)
+    k_cache: np.ndarray    # [B, Hkv, T_cap, d]
+    v_cache: np.ndarray    # [B, Hkv, T_cap, d]
+    seq_lens: np.ndarray   # [B] int32
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    cfg: PrefillConfig
+    q: np.ndarray          # [B, Hq, N, d]  (uint16 bf16 bits)
+    k: np.ndarray          # [B, Hkv, N, d]
+    v: np.ndarray          # [B, Hkv, N, d]
+
+
+def make_seq_lens(cfg: DecodeConfig, rng: Optional[np.random.Generator] = None) -> np.ndarray:
+    if rng is None:
+        rng = _streams(cfg.seed)[0]
+    if not cfg.ragged:
+        return np.full(cfg.batch, cfg.max_len, dtype=np.int32)
+    return rng.integers(cfg.min_len, cfg.max_len, endpoint=True,
+                        size=cfg.batch).astype(np.int32)
+
+
+def make_decode(cfg: DecodeConfig, poison_padding: bool = True) -> DecodeInputs:
+    """Deterministic decode inputs for ``cfg`` (see module docstring)."""
+    r_len, r_q, r_k, r_v = _streams(cfg.seed)
+    seq_lens = make_seq_lens(cfg, r_len)
+    B, Hq, Hkv, d, T = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.max_seq_len
+    q = _normals(r_q, (B, Hq, d), cfg.dtype)
+    store = np.uint16 if cfg.dtype == "bf16" else np.float32
+    k = np.empty((B, Hkv, T, d), dtype=store)
+    v = np.empty((B, Hkv, T, d), dtype=store)
+    for b in range(B):   # per sequence keeps the float32 temporaries small
+        k[b] = _normals(r_k, (Hkv, T, d), cfg.dtype)
+        v[b] = _normals(r_v, (Hkv, T, d), cfg.dtype)
+    if poison_padding:
+        poison_past_lengths(k, seq_lens, cfg.dtype)
+        poison_past_lengths(v, seq_lens, cfg.dtype)
+    return DecodeInputs(cfg, q, k, v, seq_lens)
+
+
+def poison_past_lengths(cache: np.ndarray, seq_lens: np.ndarray, dtype: str) -> None:
+    """Fill cache slots at positions >= seq_lens[b] with NaN, in place."""
+    fill = BF16_NAN_BITS if dtype == "bf16" else np.float32(np.nan)
+    for b, t in enumerate(seq_lens):
+        cache[b, :, int(t):, :] = fill
+
+
+def make_prefill(cfg: PrefillConfig) -> PrefillInputs:
+    _, r_q, r_k, r_v = _streams(cfg.seed)
+    B, Hq, Hkv, N, d = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim
+    q = _normals(r_q, (B, Hq, N, d), cfg.dtype)
+    k = _normals(r_k, (B, Hkv, N, d), cfg.dtype)
+    v = _normals(r_v, (B, Hkv, N, d), cfg.dtype)
+    return PrefillInputs(cfg, q, k, v)
+
+
+def small_decode(dtype: str, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 seq_lens, max_seq_len: int, seed: int) -> DecodeInputs:
+    """Decode inputs of an arbitrary small shape (edge cases, ragged tails)."""
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    cfg = DecodeConfig(f"small-{seed}", dtype, batch, num_q_heads, num_kv_heads, head_dim,
+                       max_seq_len, int(lens.min()) if lens.size else 0,
+                       int(lens.max()) if lens.size else 0, seed)
+    _, r_q, r_k, r_v = _streams(seed)
+    q = _normals(r_q, (batch, num_q_heads, head_dim), dtype)
+    k = _normals(r_k, (batch, num_kv_heads, max_seq_len, head_dim), dtype)
+    v = _normals(r_v, (batch, num_kv_heads, max_seq_len, head_dim), dtype)
+    poison_past_lengths(k, lens, dtype)
+    poison_past_lengths(v, lens, dtype)
+    return DecodeInputs(cfg, q, k, v, lens)
+
+
+def small_prefill(batch: int, num_q_heads: int, num_kv_heads: int, seq_len: int,
+                  head_dim: int, seed: int) -> PrefillInputs:
+    cfg = PrefillConfig(f"small-{seed}", "bf16", batch, num_q_heads, num_kv_heads,
+                        head_dim, seq_len, seed)
+    return make_prefill(cfg)

@@ -1,0 +1,58 @@
+"""Scalar brute force for tiny attention problems, in pure Python.
+
+Test infrastructure: an independent restatement of the definition used to pin
+the numpy oracle.  No arrays, no repeat, no vectorised softmax: every score is
+a plain sum of products, the KV head is picked by index (query head h reads
+KV head h // g), and sums use math.fsum.
+"""
+import math
+
+
+def _attend(qvec, keys, values, scale):
+    scores = [scale * math.fsum(a * b for a, b in zip(qvec, key)) for key in keys]
+    top = max(scores)
+    weights = [math.exp(s - top) for s in scores]
+    total = math.fsum(weights)
+    d = len(values[0])
+    return [math.fsum(w * val[c] for w, val in zip(weights, values)) / total for c in range(d)]
+
+
+def brute_decode(q, k, v, seq_lens, scale):
+    """q[b][h][i]; k, v [b][kv][t][i]; returns out[b][h][i] as nested lists."""
+    B, Hq = len(q), len(q[0])
+    Hkv = len(k[0])
+    g = Hq // Hkv
+    out = []
+    for b in range(B):
+        T = int(seq_lens[b])
+        rows = []
+        for h in range(Hq):
+            kv = h // g
+            if T == 0:
+                rows.append([0.0] * len(q[b][h]))
+                continue
+            keys = [list(k[b][kv][t]) for t in range(T)]
+            vals = [list(v[b][kv][t]) for t in range(T)]
+            rows.append(_attend(list(q[b][h]), keys, vals, scale))
+        out.append(rows)
+    return out
+
+
+def brute_prefill(q, k, v, scale):
+    """q[b][h][i][c]; k, v [b][kv][j][c]; causal (key j <= query i)."""
+    B, Hq, N = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k[0])
+    g = Hq // Hkv
+    out = []
+    for b in range(B):
+        heads = []
+        for h in range(Hq):
+            kv = h // g
+            rows = []
+            for i in range(N):
+                keys = [list(k[b][kv][j]) for j in range(i + 1)]
+                vals = [list(v[b][kv][j]) for j in range(i + 1)]
+                rows.append(_attend(list(q[b][h][i]), keys, vals, scale))
+            heads.append(rows)
+        out.append(heads)
+    return out
