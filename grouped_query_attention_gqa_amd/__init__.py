@@ -1,0 +1,227 @@
+"""Python binding of libgqa.so: grouped-query attention over a KV cache on
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/gqa.h.  PyTorch supplies device
+memory and the current stream; nothing here computes attention, and there is
+no fallback: if the library is missing, loading it raises.
+
+Functions mirror the C entry points:
+
+    gqa_decode(q, k_cache, v_cache, seq_lens, scale=None, ...)       -> out
+    gqa_decode_split(...) / gqa_decode_merge(...)                    (two stages)
+    gqa_decode_plan(batch, Hq, Hkv, d, max_seq_len, dtype, split)    -> Plan
+    gqa_prefill_causal(q, k, v, scale=None, return_lse=False)        -> out[, lse]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+__all__ = [
+    "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
+    "gqa_decode_plan", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
+    "gqa_prefill_causal", "GQA_F32", "GQA_BF16",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GQA_F32, GQA_BF16 = 0, 1
+_STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
+           4: "GQA_ERR_WORKSPACE", 5: "GQA_ERR_HIP", 6: "GQA_ERR_ALIGN"}
+
+_lib = None
+
+
+class GqaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        msg = f"{fn} failed with {_STATUS.get(status, status)}"
+        super().__init__(msg + (f": {detail}" if detail else ""))
+
+
+class Plan(NamedTuple):
+    chunk_tokens: int
+    num_splits: int
+    workspace_bytes: int
+
+
+def library_path() -> str:
+    return os.environ.get("GQA_LIBRARY", os.path.join(HERE, "libgqa.so"))
+
+
+def load_library():
+    """Load libgqa.so (built by grouped_query_attention_gqa_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m grouped_query_attention_gqa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.gqa_abi_version.restype = I32
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_status_string.argtypes = [I32]
+    lib.gqa_last_hip_error.restype = ctypes.c_char_p
+    lib.gqa_decode_plan.restype = I32
+    lib.gqa_decode_plan.argtypes = [I32] * 7 + [ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                                ctypes.POINTER(I64)]
+    lib.gqa_decode.restype = I32
+    lib.gqa_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
+    lib.gqa_decode_split.restype = I32
+    lib.gqa_decode_split.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
+    lib.gqa_decode_merge.restype = I32
+    lib.gqa_decode_merge.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
+    lib.gqa_prefill_causal.restype = I32
+    lib.gqa_prefill_causal.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P]
+    _lib = lib
+    return lib
+
+
+def gqa_abi_version() -> int:
+    return load_library().gqa_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = load_library()
+        detail = lib.gqa_last_hip_error().decode() if status == 5 else ""
+        if status in (1, 2, 3, 4, 6):
+            raise ValueError(str(GqaError(fn, status, detail)))
+        raise GqaError(fn, status, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}: expected torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*tensors: torch.Tensor):
+    dev = tensors[0].device
+    for t in tensors:
+        _require(t.is_cuda and t.device == dev, "all tensors must be on the same GPU device")
+        _require(t.is_contiguous(), "all tensors must be contiguous")
+    return dev
+
+
+def gqa_decode_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    max_seq_len: int, dtype: int, split_tokens: int = 0) -> Plan:
+    lib = load_library()
+    c, n, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check("gqa_decode_plan", lib.gqa_decode_plan(batch, num_q_heads, num_kv_heads, head_dim,
+                                                  max_seq_len, dtype, split_tokens,
+                                                  ctypes.byref(c), ctypes.byref(n), ctypes.byref(w)))
+    return Plan(c.value, n.value, w.value)
+
+
+def _decode_args(q, k_cache, v_cache, seq_lens):
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4,
+             "expected q [B,Hq,d] and k_cache/v_cache [B,Hkv,T_cap,d]")
+    _require(k_cache.shape == v_cache.shape, "k_cache and v_cache shapes differ")
+    B, Hq, d = q.shape
+    B2, Hkv, tcap, d2 = k_cache.shape
+    _require(B == B2 and d == d2, "q and cache disagree on batch or head_dim")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q, k_cache, v_cache must share a dtype")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    dev = _on_gpu(q, k_cache, v_cache, seq_lens)
+    return dev, B, Hq, Hkv, tcap, d, _dtype_code(q)
+
+
+def _workspace(workspace, plan: Plan, dev):
+    if workspace is None:
+        return torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    _require(workspace.is_cuda and workspace.device == dev and workspace.is_contiguous(),
+             "workspace must be a contiguous tensor on the same device")
+    return workspace
+
+
+def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               seq_lens: torch.Tensor, scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               split_tokens: int = 0) -> torch.Tensor:
+    """One GQA decode step; returns out [B, Hq, d] float32 (see gqa.h)."""
+    dev, B, Hq, Hkv, tcap, d, dt = _decode_args(q, k_cache, v_cache, seq_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    plan = gqa_decode_plan(B, Hq, Hkv, d, tcap, dt, split_tokens)
+    ws = _workspace(workspace, plan, dev)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, d), "out must be float32 [B,Hq,d]")
+    _on_gpu(q, out)
+    lib = load_library()
+    _check("gqa_decode", lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                        _ptr(out), B, Hq, Hkv, d, tcap, scale, dt, split_tokens,
+                                        _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def gqa_decode_split(q, k_cache, v_cache, seq_lens, workspace, scale=None, split_tokens=0):
+    """Stage 1 of decode: chunk partials into ``workspace`` (uint8 tensor)."""
+    dev, B, Hq, Hkv, tcap, d, dt = _decode_args(q, k_cache, v_cache, seq_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _workspace(workspace, Plan(0, 0, 0), dev)
+    lib = load_library()
+    _check("gqa_decode_split", lib.gqa_decode_split(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, d, tcap, scale, dt,
+        split_tokens, _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def gqa_decode_merge(seq_lens, out, workspace, num_kv_heads, max_seq_len, dtype, split_tokens=0):
+    """Stage 2 of decode: merge the partials in ``workspace`` into ``out``."""
+    dev = _on_gpu(seq_lens, out, workspace)
+    B, Hq, d = out.shape
+    _require(out.dtype == torch.float32, "out must be float32")
+    lib = load_library()
+    _check("gqa_decode_merge", lib.gqa_decode_merge(
+        _ptr(seq_lens), _ptr(out), B, Hq, num_kv_heads, d, max_seq_len, dtype, split_tokens,
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def gqa_prefill_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       return_lse: bool = False, lse: Optional[torch.Tensor] = None):
+    """Causal GQA prefill; returns out [B, Hq, N, d] float32 (and lse)."""
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "expected 4-d q, k, v")
+    _require(k.shape == v.shape, "k and v shapes differ")
+    B, Hq, N, d = q.shape
+    B2, Hkv, N2, d2 = k.shape
+    _require(B == B2 and N == N2 and d == d2, "q and k/v disagree on batch, length or head_dim")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    dev = _on_gpu(q, k, v)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _require(lse.dtype == torch.float32 and lse.shape == (B, Hq, N), "lse must be float32 [B,Hq,N]")
+        _on_gpu(q, lse)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, N, d), "out must be float32 [B,Hq,N,d]")
+    _on_gpu(q, out)
+    lib = load_library()
+    _check("gqa_prefill_causal", lib.gqa_prefill_causal(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale, dt, _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out

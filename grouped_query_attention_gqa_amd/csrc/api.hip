@@ -1,0 +1,211 @@
+// C ABI of libgqa.so (declared in include/gqa.h): argument validation, split
+// planning and kernel launches.  Validation is pure host arithmetic done
+// before any HIP call, so every error path is reachable without a GPU.
+
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "gqa.h"
+#include "gqa_launch.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return GQA_OK;
+  const char* s = hipGetErrorString(e);
+  strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return GQA_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workgroups the automatic split aims for: enough resident waves across the
+// 256 CUs of an MI355X to keep HBM saturated (4 waves each).
+constexpr int64_t kTargetWorkgroups = 1024;
+// Smallest automatic split: keeps the partials (and merge work) a few
+// percent of the KV bytes.
+constexpr int64_t kMinAutoChunk = 1024;
+
+int32_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return GQA_ERR_SHAPE;
+  if (d != 64 && d != 128) return GQA_ERR_UNSUPPORTED;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tcap, int32_t dtype,
+                  int32_t split_tokens, float scale, gqa::DecodeShape* s) {
+  int32_t st = check_heads(batch, hq, hkv, d, dtype);
+  if (st != GQA_OK) return st;
+  if (tcap < 1) return GQA_ERR_SHAPE;
+  // Every tensor must be addressable with 64-bit element offsets and the
+  // grid must fit the launch limits.
+  const int64_t kv_elems = (int64_t)batch * hkv * (int64_t)tcap * d;
+  if (kv_elems / d / tcap / hkv != batch || kv_elems > (INT64_MAX / 8)) return GQA_ERR_SHAPE;
+  const int64_t g = hq / hkv;
+  const int64_t nhb = (g + gqa::kDecodeHeadBlock - 1) / gqa::kDecodeHeadBlock;
+  int64_t chunk;
+  if (split_tokens == 0) {
+    const int64_t units = (int64_t)batch * hkv * nhb;
+    int64_t per = (units * (int64_t)tcap + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    if (per < kMinAutoChunk) per = kMinAutoChunk;
+    const int64_t cap = ((int64_t)tcap + gqa::kSplitQuantum - 1) / gqa::kSplitQuantum * gqa::kSplitQuantum;
+    chunk = (per + 255) / 256 * 256;
+    if (chunk > cap) chunk = cap;
+  } else {
+    if (split_tokens < 0 || split_tokens % gqa::kSplitQuantum != 0) return GQA_ERR_UNSUPPORTED;
+    chunk = split_tokens;
+  }
+  const int64_t nsplit = ((int64_t)tcap + chunk - 1) / chunk;
+  if (nsplit > INT32_MAX || (int64_t)hkv * nhb > 65535 || batch > 65535) return GQA_ERR_SHAPE;
+  s->batch = batch;
+  s->hq = hq;
+  s->hkv = hkv;
+  s->d = d;
+  s->tcap = tcap;
+  s->chunk = (int)chunk;
+  s->nsplit = (int)nsplit;
+  s->scale = scale;
+  s->dtype = dtype;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char* gqa_status_string(int32_t status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_NULL: return "GQA_ERR_NULL";
+    case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN";
+    default: return "GQA_ERR_UNKNOWN";
+  }
+}
+
+const char* gqa_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_seq_len, int32_t dtype,
+                        int32_t split_tokens, int32_t* chunk_tokens_out,
+                        int32_t* num_splits_out, int64_t* workspace_bytes_out) {
+  gqa::DecodeShape s;
+  const int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, dtype,
+                               split_tokens, 1.f, &s);
+  if (st != GQA_OK) return st;
+  if (chunk_tokens_out) *chunk_tokens_out = s.chunk;
+  if (num_splits_out) *num_splits_out = s.nsplit;
+  if (workspace_bytes_out) *workspace_bytes_out = gqa::decode_workspace_layout(s).total;
+  return GQA_OK;
+}
+
+static int32_t decode_prepare(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, const void* workspace,
+                              int64_t workspace_bytes, int32_t batch, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t tcap, float scale, int32_t dtype,
+                              int32_t split_tokens, gqa::DecodeShape* s,
+                              gqa::DecodeWorkspace* ws) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !workspace) return GQA_ERR_NULL;
+  const int32_t st = make_plan(batch, hq, hkv, d, tcap, dtype, split_tokens, scale, s);
+  if (st != GQA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) ||
+      !aligned(seq_lens, 4))
+    return GQA_ERR_ALIGN;
+  *ws = gqa::decode_workspace_layout(*s);
+  if (workspace_bytes < ws->total) return GQA_ERR_WORKSPACE;
+  return GQA_OK;
+}
+
+int32_t gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                         float scale, int32_t dtype, int32_t split_tokens, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  gqa::DecodeShape s;
+  gqa::DecodeWorkspace ws;
+  const int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch,
+                                    num_q_heads, num_kv_heads, head_dim, max_seq_len, scale, dtype,
+                                    split_tokens, &s, &ws);
+  if (st != GQA_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  return hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens,
+                                             reinterpret_cast<float*>(base + ws.o_offset),
+                                             reinterpret_cast<float*>(base + ws.lse_offset), s,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t gqa_decode_merge(const int32_t* seq_lens, float* out, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                         int32_t dtype, int32_t split_tokens, const void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (!seq_lens || !out || !workspace) return GQA_ERR_NULL;
+  gqa::DecodeShape s;
+  const int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, dtype,
+                               split_tokens, 1.f, &s);
+  if (st != GQA_OK) return st;
+  if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(seq_lens, 4)) return GQA_ERR_ALIGN;
+  const gqa::DecodeWorkspace ws = gqa::decode_workspace_layout(s);
+  if (workspace_bytes < ws.total) return GQA_ERR_WORKSPACE;
+  const char* base = static_cast<const char*>(workspace);
+  return hip_status(gqa::launch_decode_merge(reinterpret_cast<const float*>(base + ws.o_offset),
+                                             reinterpret_cast<const float*>(base + ws.lse_offset),
+                                             seq_lens, out, s, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seq_lens, float* out, int32_t batch, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len, float scale,
+                   int32_t dtype, int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  if (!out) return GQA_ERR_NULL;
+  gqa::DecodeShape s;
+  gqa::DecodeWorkspace ws;
+  int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch,
+                              num_q_heads, num_kv_heads, head_dim, max_seq_len, scale, dtype,
+                              split_tokens, &s, &ws);
+  if (st != GQA_OK) return st;
+  if (!aligned(out, 16)) return GQA_ERR_ALIGN;
+  char* base = static_cast<char*>(workspace);
+  float* po = reinterpret_cast<float*>(base + ws.o_offset);
+  float* pl = reinterpret_cast<float*>(base + ws.lse_offset);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, po, pl, s, hs));
+  if (st != GQA_OK) return st;
+  return hip_status(gqa::launch_decode_merge(po, pl, seq_lens, out, s, hs));
+}
+
+int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out, float* lse,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t seq_len, int32_t head_dim, float scale, int32_t dtype,
+                           void* stream) {
+  if (!q || !k || !v || !out) return GQA_ERR_NULL;
+  int32_t st = check_heads(batch, num_q_heads, num_kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (seq_len < 1) return GQA_ERR_SHAPE;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  const int64_t q_elems = (int64_t)batch * num_q_heads * (int64_t)seq_len * head_dim;
+  if (q_elems / head_dim / seq_len / num_q_heads != batch || q_elems > (INT64_MAX / 8))
+    return GQA_ERR_SHAPE;
+  const int64_t g = num_q_heads / num_kv_heads;
+  const int64_t gw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int64_t tiles = (seq_len + 128 / gw - 1) / (128 / gw);
+  if ((int64_t)batch * num_kv_heads * (g / gw) * tiles > INT32_MAX) return GQA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return GQA_ERR_ALIGN;
+  gqa::PrefillShape s{batch, num_q_heads, num_kv_heads, seq_len, head_dim, scale};
+  return hip_status(gqa::launch_prefill_causal(q, k, v, out, lse, s, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

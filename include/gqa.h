@@ -1,0 +1,165 @@
+/*
+ * gqa.h - C ABI of libgqa.so: grouped-query attention (GQA) over a KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A layer has Hq query heads and Hkv key/value heads, with
+ * Hkv >= 1 dividing Hq; g = Hq / Hkv query heads form a group, and query
+ * head h reads KV head h / g (integer division), i.e. consecutive blocks of
+ * g query heads share one KV head (study.greatitself.com, "Grouped-Query and
+ * Multi-Query Attention", section "Share keys and values without confusing
+ * query-head identity"; lihaoran.work, section "Shared KV can still produce
+ * different outputs").  For every query head the output is
+ *
+ *     out[h] = sum_t softmax_t(scale * q[h] . K[h/g, t]) * V[h/g, t]
+ *
+ * with its own distribution per query head.  The shared K/V rows are read in
+ * place, once per group of query heads, and never copied per query head
+ * (anrans.github.io, "Attention variants: MQA, GQA, MLA", section "Kernels do
+ * not need to copy the KV heads").  MHA is Hkv = Hq and MQA is Hkv = 1.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Tensors are dense, row-major,
+ *    head-major, with the shapes written next to each argument.
+ *  - q, k, v, out and the workspace must be 16-byte aligned; lse and seq_lens
+ *    4-byte aligned.
+ *  - dtype selects the element type of q, k and v (gqa_dtype).  Outputs are
+ *    always float32 (fp32 accumulation of bf16 products).
+ *  - stream is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    validate and enqueue; they return before the GPU work finishes, and a
+ *    fault during execution surfaces at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call, so a bad call
+ *    returns an error status and enqueues nothing.  Statuses are gqa_status
+ *    values returned as int32_t; nothing is printed and nothing throws.
+ *  - The library keeps no state besides a thread-local copy of the last HIP
+ *    error text, so it is reentrant; two calls that share a workspace must
+ *    be ordered on one stream.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  GQA_ERR_SHAPE = 2,       /* size < 1, Hkv not dividing Hq, or size overflow    */
+  GQA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype not allowed, bad split  */
+  GQA_ERR_WORKSPACE = 4,   /* workspace smaller than gqa_decode_plan requires    */
+  GQA_ERR_HIP = 5,         /* the HIP runtime rejected a launch                  */
+  GQA_ERR_ALIGN = 6        /* a pointer violates the alignment rule above        */
+} gqa_status;
+
+typedef enum gqa_dtype {
+  GQA_F32 = 0,  /* IEEE float32                          */
+  GQA_BF16 = 1  /* bfloat16 (upper half of a float32)     */
+} gqa_dtype;
+
+/* Version of this ABI (GQA_ABI_VERSION). */
+int32_t gqa_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("GQA_OK", ...). */
+const char* gqa_status_string(int32_t status);
+
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char* gqa_last_hip_error(void);
+
+/*
+ * Split plan of a decode call.  Decode cuts every sequence's cached tokens
+ * into chunks of *chunk_tokens_out tokens (the last one ragged); one
+ * workgroup attends one chunk for one KV head and all query heads of its
+ * group, and the chunk results are merged by log-sum-exp.  This split is an
+ * implementation choice, not something the pages specify.
+ *
+ * split_tokens: 0 chooses the chunk automatically from the shape; otherwise
+ *   a positive multiple of 64 (GQA_ERR_UNSUPPORTED if not).
+ * Outputs (any may be NULL): chunk size in tokens, number of chunk slots per
+ *   sequence (ceil(max_seq_len / chunk)), and the workspace bytes that
+ *   gqa_decode / gqa_decode_split / gqa_decode_merge need for this shape.
+ * Pure host arithmetic: never touches the GPU.
+ */
+int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_seq_len, int32_t dtype,
+                        int32_t split_tokens, int32_t* chunk_tokens_out,
+                        int32_t* num_splits_out, int64_t* workspace_bytes_out);
+
+/*
+ * One decode step of GQA over a KV cache: every query head of every sequence
+ * attends to the first seq_lens[b] cached tokens of its KV head.
+ *
+ *   q         [batch, num_q_heads, head_dim]                     dtype
+ *   k_cache   [batch, num_kv_heads, max_seq_len, head_dim]       dtype
+ *   v_cache   [batch, num_kv_heads, max_seq_len, head_dim]       dtype
+ *   seq_lens  [batch] int32, device memory, never read on the host; values
+ *             are clamped to [0, max_seq_len]; slots past seq_lens[b] are
+ *             never used (they may hold garbage, NaN included).  A length of
+ *             0 gives an all-zero output row.
+ *   out       [batch, num_q_heads, head_dim] float32
+ *   scale     multiplies q . k (1/sqrt(head_dim) for standard attention)
+ *   dtype     GQA_F32 or GQA_BF16; head_dim 64 or 128
+ *   workspace device scratch of at least the bytes gqa_decode_plan reports
+ *             (its contents on entry do not matter; they are overwritten)
+ *
+ * Runs gqa_decode_split then gqa_decode_merge on the same stream.
+ */
+int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seq_lens, float* out, int32_t batch,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t max_seq_len, float scale, int32_t dtype,
+                   int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
+/*
+ * First stage of gqa_decode: attention of every (sequence, chunk, query
+ * head) written as a normalised partial output and its log-sum-exp into the
+ * workspace.  Arguments as for gqa_decode, without out.  Exposed so that
+ * chunk partials can be produced in one place and merged in another (for
+ * example after gathering them from several devices).
+ */
+int32_t gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                         float scale, int32_t dtype, int32_t split_tokens,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Second stage of gqa_decode: combine the chunk partials of every (sequence,
+ * query head) held in the workspace into out [batch, num_q_heads, head_dim]
+ * float32, weighting chunk c by exp(lse_c - max_c lse_c).  The shape
+ * arguments must equal those of the gqa_decode_split call that filled the
+ * workspace.
+ */
+int32_t gqa_decode_merge(const int32_t* seq_lens, float* out, int32_t batch,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_seq_len, int32_t dtype, int32_t split_tokens,
+                         const void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Causal GQA over a whole prompt (prefill): query row i of head h attends to
+ * keys 0..i of KV head h / g (lower-triangular mask broadcast over the
+ * group; anrans.github.io, "Kernels do not need to copy the KV heads").
+ *
+ *   q    [batch, num_q_heads, seq_len, head_dim]   bf16
+ *   k, v [batch, num_kv_heads, seq_len, head_dim]  bf16
+ *   out  [batch, num_q_heads, seq_len, head_dim]   float32
+ *   lse  [batch, num_q_heads, seq_len] float32 natural log-sum-exp of the
+ *        scaled scores of each row, or NULL to skip it
+ *   dtype must be GQA_BF16; head_dim 64 or 128.
+ */
+int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out,
+                           float* lse, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t seq_len, int32_t head_dim,
+                           float scale, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

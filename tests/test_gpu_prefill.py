@@ -1,0 +1,93 @@
+"""GPU causal prefill (bf16 MFMA kernel through the C ABI) against the oracle."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import grouped_query_attention_gqa_amd as gqa
+import oracle
+from gpu_util import TOL, dev, max_err, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(p):
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    out, lse = gqa.gqa_prefill_causal(q, k, v, scale=p.cfg.scale, return_lse=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d
+    (1, 8, 2, 300, 128),     # group 4, ragged tail
+    (2, 8, 2, 64, 64),
+    (1, 4, 4, 130, 128),     # MHA endpoint
+    (1, 6, 2, 77, 128),      # group 3: one head per workgroup
+    (1, 16, 1, 200, 128),    # MQA, group 16
+    (1, 4, 2, 1, 128),       # a single token
+    (1, 8, 4, 33, 64),       # group 2
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}-{}on{}-N{}-d{}".format(*c))
+def test_small_full_parity(case):
+    need_gpu()
+    B, Hq, Hkv, N, d = case
+    p = gi.small_prefill(B, Hq, Hkv, N, d, seed=zlib.crc32(repr(case).encode()) % 100000)
+    say("prefill small", case)
+    out, lse = run_prefill(p)
+    ref, ref_lse = oracle.prefill_causal(gi.to_f64(p.q, "bf16"), gi.to_f64(p.k, "bf16"),
+                                         gi.to_f64(p.v, "bf16"), p.cfg.scale, return_lse=True)
+    err, lerr = max_err(out, ref), max_err(lse, ref_lse)
+    say("max err", err, "lse err", lerr)
+    assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
+    # row 0 attends only key 0: exactly V[0]
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(out[b, h, 0], gi.bf16_bits_to_f32(p.v[b, h // g, 0]))
+
+
+def test_c5_full_size_sampled_rows():
+    need_gpu()
+    cfg = gi.CONFIGS["c5"]
+    p = gi.make_prefill(cfg)
+    say("c5", gi.describe(cfg))
+    out, lse = run_prefill(p)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 31, 32, 33, 127, 128, 129, 2047, 4094, 4095] +
+                      rng.integers(0, 4096, 8).tolist()))
+    worst = 0.0
+    for b in range(cfg.batch):
+        kb, vb = gi.to_f64(p.k[b], "bf16"), gi.to_f64(p.v[b], "bf16")
+        for h in range(cfg.num_q_heads):
+            ref, ref_lse = oracle.prefill_causal_rows(gi.to_f64(p.q[b, h, rows], "bf16"), kb, vb, rows,
+                                                      h, cfg.num_q_heads, cfg.scale)
+            worst = max(worst, max_err(out[b, h, rows], ref), max_err(lse[b, h, rows], ref_lse))
+    say("c5 sampled max err", worst)
+    assert worst <= TOL["bf16"]
+
+
+def test_causality_perturbation_bit_identical():
+    need_gpu()
+    p = gi.small_prefill(1, 8, 2, 256, 128, seed=31)
+    out_a, _ = run_prefill(p)
+    i = 100
+    p.k[:, :, i + 1:] = gi.f32_to_bf16_bits(gi.bf16_bits_to_f32(p.k[:, :, i + 1:]) * 2.0 + 1.0)
+    p.v[:, :, i + 1:] = gi.f32_to_bf16_bits(gi.bf16_bits_to_f32(p.v[:, :, i + 1:]) - 3.0)
+    out_b, _ = run_prefill(p)
+    assert np.array_equal(out_a[:, :, :i + 1], out_b[:, :, :i + 1])
+    assert not np.allclose(out_a[:, :, i + 1:], out_b[:, :, i + 1:])
+
+
+def test_identical_queries_in_group_identical_rows():
+    need_gpu()
+    p = gi.small_prefill(1, 4, 1, 96, 128, seed=41)
+    p.q[:, 1] = p.q[:, 0]
+    out, _ = run_prefill(p)
+    assert np.array_equal(out[0, 0], out[0, 1])
+    assert not np.allclose(out[0, 0], out[0, 2])
