@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA hot path on one MI355X.
+
+Default workload (one JSON line on stdout):
+  decode, Llama-3-8B-shaped layer: B=32, Hq=32, Hkv=8, d=128, 8192 cached
+  tokens per sequence, bf16 cache, fp32 accumulation.  A step is one full
+  decode call (split kernel + log-sum-exp merge) over the whole batch.
+  value = KV-cache bytes read per step / step time (GB/s).
+  The same run also times causal prefill (B=2, Hq=32, Hkv=8, N=4096, d=128)
+  and reports its TFLOP/s in the "prefill" object.
+
+Inputs are seeded synthetic N(0,1) values; K/V are resident in HBM before the
+timed region and rotated over several copies so the 256 MB MALL cannot serve
+repeated steps.  Kernel durations come from HIP events on the stream the
+kernels run on (torch's current stream, which the binding launches on).
+
+  python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "GQA decode KV-read GB/s (% of HBM peak) + causal prefill TFLOP/s (% MFMA)"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", f)
+                  for f in ("decode.hip", "prefill.hip", "gqa_device.hpp", "gqa_launch.hpp")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (the bytes and FLOPs the method itself must move / do)
+# ---------------------------------------------------------------------------
+
+def decode_kv_bytes(seq_lens, hkv, d, elem):
+    """K and V of every attended token: 2 * sum(T_b) * Hkv * d * elem."""
+    return 2 * int(np.sum(seq_lens, dtype=np.int64)) * hkv * d * elem
+
+
+def decode_split_bytes(seq_lens, hq, hkv, d, elem):
+    """Algorithmic bytes of the split kernel: the attended K/V plus q."""
+    return decode_kv_bytes(seq_lens, hkv, d, elem) + len(seq_lens) * hq * d * elem
+
+
+def decode_flops(seq_lens, hq, d):
+    return 4 * hq * d * int(np.sum(seq_lens, dtype=np.int64))
+
+
+def prefill_flops(b, hq, n, d):
+    """Exact causal count: row i attends i+1 keys at 4*d FLOPs per key."""
+    return 4 * b * hq * d * n * (n + 1) // 2
+
+
+def prefill_bytes(b, hq, hkv, n, d):
+    """q, k, v in bf16 and the fp32 output."""
+    return b * n * d * (2 * hq + 2 * 2 * hkv + 4 * hq)
+
+
+# ---------------------------------------------------------------------------
+
+def event_time_ms(fn, iters, torch):
+    """Average duration of fn() over `iters` back-to-back calls, by HIP events
+    on the current stream."""
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(iters):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def load_counters(kernel: str, workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, only if
+    the kernel sources are unchanged since they were taken."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(f"{kernel}|{workload}")
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def cpu_baseline_decode(inp, budget_s: float):
+    """Time the float64 oracle on the host over as many whole sequences of
+    the workload as fit in about `budget_s` seconds."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import gqa_inputs as gi
+    import oracle
+    cores = min(16, len(os.sched_getaffinity(0)))
+    cfg = inp.cfg
+    done, t_used, bytes_done = 0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        for b in range(cfg.batch):
+            q = gi.to_f64(inp.q[b:b + 1], cfg.dtype)
+            k = inp.k_cache[b:b + 1]
+            v = inp.v_cache[b:b + 1]
+            t0 = time.perf_counter()
+            kf = gi.to_f64(k, cfg.dtype)
+            vf = gi.to_f64(v, cfg.dtype)
+            oracle.decode(q, kf, vf, inp.seq_lens[b:b + 1], cfg.scale)
+            t_used += time.perf_counter() - t0
+            done += 1
+            bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim,
+                                          2 if cfg.dtype == "bf16" else 4)
+            if t_used >= budget_s:
+                break
+    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of the same workload (float64 numpy oracle, "
+                      f"explicit K/V repeat), {t_used:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4"])
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain device copy of 256 MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GQA kernels here run on a single device "
+              "and no multi-GPU path is built; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_inputs as gi
+    import grouped_query_attention_gqa_amd as gqa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gqa.load_library()   # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    cfg = gi.CONFIGS[args.workload]
+    inp = gi.make_decode(cfg)
+    elem = 2 if cfg.dtype == "bf16" else 4
+    dt = gqa.GQA_BF16 if cfg.dtype == "bf16" else gqa.GQA_F32
+    B, Hq, Hkv, d, T = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.max_seq_len
+    kv_bytes = decode_kv_bytes(inp.seq_lens, Hkv, d, elem)
+    alloc_kv = 2 * B * Hkv * T * d * elem
+    rot = max(2, math.ceil(4 * MALL_BYTES / alloc_kv))
+
+    def to_dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q = to_dev(inp.q)
+    k0, v0 = to_dev(inp.k_cache), to_dev(inp.v_cache)
+    ks = [k0] + [k0.clone() for _ in range(rot - 1)]
+    vs = [v0] + [v0.clone() for _ in range(rot - 1)]
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    plan = gqa.gqa_decode_plan(B, Hq, Hkv, d, T, dt, args.split_tokens)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        gqa.gqa_decode(q, ks[i % rot], vs[i % rot], lens, scale=cfg.scale, out=out, workspace=ws,
+                       split_tokens=args.split_tokens)
+
+    def split_only(i):
+        gqa.gqa_decode_split(q, ks[i % rot], vs[i % rot], lens, ws, scale=cfg.scale,
+                             split_tokens=args.split_tokens)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = event_time_ms(step, args.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_split = event_time_ms(split_only, args.steps, torch)
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    split_bytes = decode_split_bytes(inp.seq_lens, Hq, Hkv, d, elem)
+    achieved = split_bytes / (ms_split * 1e-3) / 1e9
+    traffic = load_counters("decode_split", args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": gi.describe(cfg), "global_batch": B, "seq_len": T,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
+                   "split_tokens": plan.chunk_tokens, "num_splits": plan.num_splits,
+                   "kv_rotation_copies": rot, "parallelism": "single-gpu"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_tflops": round(decode_flops(inp.seq_lens, Hq, d) / (ms_step * 1e-3) / 1e12, 3),
+        "roofline": {"kernel": "decode_split_bf16" if cfg.dtype == "bf16" else "decode_split_f32",
+                     "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": split_bytes,
+                     "ms_per_launch": round(ms_split, 5)},
+        "timed_wall_s": round(wall, 4),
+    }
+
+    if not args.no_prefill:
+        pc = gi.CONFIGS["c5"]
+        p = gi.make_prefill(pc)
+        pq, pk, pv = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (p.q, p.k, p.v))
+        pout = torch.empty(pc.batch, pc.num_q_heads, pc.seq_len, pc.head_dim, dtype=torch.float32,
+                           device="cuda")
+
+        def pstep(i):
+            gqa.gqa_prefill_causal(pq, pk, pv, scale=pc.scale, out=pout)
+
+        for i in range(max(3, args.warmup // 2)):
+            pstep(i)
+        pms = event_time_ms(pstep, max(10, args.steps // 2), torch)
+        fl = prefill_flops(pc.batch, pc.num_q_heads, pc.seq_len, pc.head_dim)
+        tf = fl / (pms * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": gi.describe(pc), "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_call": round(pms, 5), "tokens_per_s": round(pc.batch * pc.seq_len / (pms * 1e-3), 1),
+            "pct_of_mfma_peak": round(100 * tf / BF16_MFMA_PEAK_TFLOPS, 2),
+            "roofline": {"kernel": "prefill_causal_bf16", "bound": "mfma", "achieved": round(tf, 2),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": load_counters("prefill_causal", "c5"),
+                         "algorithmic_flops": fl,
+                         "algorithmic_bytes": prefill_bytes(pc.batch, pc.num_q_heads, pc.num_kv_heads,
+                                                            pc.seq_len, pc.head_dim)},
+        }
+
+    if args.calibration_copy:
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
