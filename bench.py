@@ -192,7 +192,7 @@ def main():
                        split_tokens=args.split_tokens)
 
     def split_only(i):
-        gqa.gqa_decode_split(q, ks[i % rot], vs[i % rot], lens, ws, scale=cfg.scale,
+        gqa.gqa_decode_split(q, ks[i % rot], vs[i % rot], lens, out, ws, scale=cfg.scale,
                              split_tokens=args.split_tokens)
 
     for i in range(args.warmup):
@@ -223,7 +223,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": gi.describe(cfg), "global_batch": B, "seq_len": T,
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
-                   "split_tokens": plan.chunk_tokens, "num_splits": plan.num_splits,
+                   "range_tokens": plan.range_tokens or "auto", "workgroups": plan.workgroups,
                    "kv_rotation_copies": rot, "parallelism": "single-gpu"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),

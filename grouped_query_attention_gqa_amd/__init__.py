@@ -44,8 +44,8 @@ class GqaError(RuntimeError):
 
 
 class Plan(NamedTuple):
-    chunk_tokens: int
-    num_splits: int
+    range_tokens: int      # fixed range size, 0 = chosen on the device
+    workgroups: int        # workgroups the split kernel launches
     workspace_bytes: int
 
 
@@ -74,7 +74,7 @@ def load_library():
     lib.gqa_decode.restype = I32
     lib.gqa_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
     lib.gqa_decode_split.restype = I32
-    lib.gqa_decode_split.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
+    lib.gqa_decode_split.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
     lib.gqa_decode_merge.restype = I32
     lib.gqa_decode_merge.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
     lib.gqa_prefill_causal.restype = I32
@@ -176,15 +176,19 @@ def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
-def gqa_decode_split(q, k_cache, v_cache, seq_lens, workspace, scale=None, split_tokens=0):
-    """Stage 1 of decode: chunk partials into ``workspace`` (uint8 tensor)."""
+def gqa_decode_split(q, k_cache, v_cache, seq_lens, out, workspace, scale=None, split_tokens=0):
+    """Stage 1 of decode: final rows of single-range sequences into ``out``,
+    partials of the others into ``workspace`` (uint8 tensor)."""
     dev, B, Hq, Hkv, tcap, d, dt = _decode_args(q, k_cache, v_cache, seq_lens)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _workspace(workspace, Plan(0, 0, 0), dev)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, d), "out must be float32 [B,Hq,d]")
+    _on_gpu(q, out)
     lib = load_library()
     _check("gqa_decode_split", lib.gqa_decode_split(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, d, tcap, scale, dt,
-        split_tokens, _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, tcap,
+        scale, dt, split_tokens, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
 
 
 def gqa_decode_merge(seq_lens, out, workspace, num_kv_heads, max_seq_len, dtype, split_tokens=0):

@@ -24,13 +24,6 @@ int32_t hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Workgroups the automatic split aims for: enough resident waves across the
-// 256 CUs of an MI355X to keep HBM saturated (4 waves each).
-constexpr int64_t kTargetWorkgroups = 1024;
-// Smallest automatic split: keeps the partials (and merge work) a few
-// percent of the KV bytes.
-constexpr int64_t kMinAutoChunk = 1024;
-
 int32_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
   if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return GQA_ERR_SHAPE;
   if (d != 64 && d != 128) return GQA_ERR_UNSUPPORTED;
@@ -38,38 +31,45 @@ int32_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t d
   return GQA_OK;
 }
 
+// Decode launch plan: the work is one stream of (unit, token) pairs cut into
+// equal ranges (see decode.hip).  With split_tokens == 0 the range size is
+// picked on the device from the actual lengths for kPersistentWorkgroups
+// resident workgroups; otherwise it is split_tokens.
 int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tcap, int32_t dtype,
                   int32_t split_tokens, float scale, gqa::DecodeShape* s) {
   int32_t st = check_heads(batch, hq, hkv, d, dtype);
   if (st != GQA_OK) return st;
   if (tcap < 1) return GQA_ERR_SHAPE;
-  // Every tensor must be addressable with 64-bit element offsets and the
-  // grid must fit the launch limits.
+  if (split_tokens < 0 || split_tokens % gqa::kRangeQuantum != 0) return GQA_ERR_UNSUPPORTED;
+  // Element offsets are 64-bit; buffer offsets inside one segment are
+  // 32-bit, so one sequence's cache row must stay below 2 GiB.
   const int64_t kv_elems = (int64_t)batch * hkv * (int64_t)tcap * d;
   if (kv_elems / d / tcap / hkv != batch || kv_elems > (INT64_MAX / 8)) return GQA_ERR_SHAPE;
+  if ((int64_t)tcap * d * 4 > INT32_MAX) return GQA_ERR_SHAPE;
   const int64_t g = hq / hkv;
   const int64_t nhb = (g + gqa::kDecodeHeadBlock - 1) / gqa::kDecodeHeadBlock;
-  int64_t chunk;
+  const int64_t units = (int64_t)batch * hkv * nhb;
+  const int64_t work = units * (int64_t)tcap;   // upper bound on token-units
+  int64_t ranges, grid;
   if (split_tokens == 0) {
-    const int64_t units = (int64_t)batch * hkv * nhb;
-    int64_t per = (units * (int64_t)tcap + kTargetWorkgroups - 1) / kTargetWorkgroups;
-    if (per < kMinAutoChunk) per = kMinAutoChunk;
-    const int64_t cap = ((int64_t)tcap + gqa::kSplitQuantum - 1) / gqa::kSplitQuantum * gqa::kSplitQuantum;
-    chunk = (per + 255) / 256 * 256;
-    if (chunk > cap) chunk = cap;
+    grid = (work + gqa::kMinRange - 1) / gqa::kMinRange;
+    if (grid > gqa::kPersistentWorkgroups) grid = gqa::kPersistentWorkgroups;
+    ranges = grid;   // the device picks Q >= W / grid
   } else {
-    if (split_tokens < 0 || split_tokens % gqa::kSplitQuantum != 0) return GQA_ERR_UNSUPPORTED;
-    chunk = split_tokens;
+    ranges = (work + split_tokens - 1) / split_tokens;
+    grid = ranges < gqa::kPersistentWorkgroups ? ranges : gqa::kPersistentWorkgroups;
   }
-  const int64_t nsplit = ((int64_t)tcap + chunk - 1) / chunk;
-  if (nsplit > INT32_MAX || (int64_t)hkv * nhb > 65535 || batch > 65535) return GQA_ERR_SHAPE;
+  const int64_t slots = ranges + units;
+  if (units > INT32_MAX || slots > INT32_MAX / gqa::kDecodeHeadBlock) return GQA_ERR_SHAPE;
   s->batch = batch;
   s->hq = hq;
   s->hkv = hkv;
   s->d = d;
   s->tcap = tcap;
-  s->chunk = (int)chunk;
-  s->nsplit = (int)nsplit;
+  s->units = (int)units;
+  s->q_fixed = split_tokens;
+  s->grid = (int)grid;
+  s->max_slots = slots;
   s->scale = scale;
   s->dtype = dtype;
   return GQA_OK;
@@ -98,14 +98,14 @@ const char* gqa_last_hip_error(void) { return g_last_hip_error; }
 
 int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_seq_len, int32_t dtype,
-                        int32_t split_tokens, int32_t* chunk_tokens_out,
-                        int32_t* num_splits_out, int64_t* workspace_bytes_out) {
+                        int32_t split_tokens, int32_t* range_tokens_out,
+                        int32_t* workgroups_out, int64_t* workspace_bytes_out) {
   gqa::DecodeShape s;
   const int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, dtype,
                                split_tokens, 1.f, &s);
   if (st != GQA_OK) return st;
-  if (chunk_tokens_out) *chunk_tokens_out = s.chunk;
-  if (num_splits_out) *num_splits_out = s.nsplit;
+  if (range_tokens_out) *range_tokens_out = s.q_fixed;
+  if (workgroups_out) *workgroups_out = s.grid;
   if (workspace_bytes_out) *workspace_bytes_out = gqa::decode_workspace_layout(s).total;
   return GQA_OK;
 }
@@ -128,20 +128,20 @@ static int32_t decode_prepare(const void* q, const void* k_cache, const void* v_
 }
 
 int32_t gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                         const int32_t* seq_lens, float* out, int32_t batch, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                          float scale, int32_t dtype, int32_t split_tokens, void* workspace,
                          int64_t workspace_bytes, void* stream) {
+  if (!out) return GQA_ERR_NULL;
   gqa::DecodeShape s;
   gqa::DecodeWorkspace ws;
   const int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch,
                                     num_q_heads, num_kv_heads, head_dim, max_seq_len, scale, dtype,
                                     split_tokens, &s, &ws);
   if (st != GQA_OK) return st;
-  char* base = static_cast<char*>(workspace);
-  return hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens,
-                                             reinterpret_cast<float*>(base + ws.o_offset),
-                                             reinterpret_cast<float*>(base + ws.lse_offset), s,
+  if (!aligned(out, 16)) return GQA_ERR_ALIGN;
+  return hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, out,
+                                             static_cast<char*>(workspace), s,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -157,10 +157,8 @@ int32_t gqa_decode_merge(const int32_t* seq_lens, float* out, int32_t batch, int
   if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(seq_lens, 4)) return GQA_ERR_ALIGN;
   const gqa::DecodeWorkspace ws = gqa::decode_workspace_layout(s);
   if (workspace_bytes < ws.total) return GQA_ERR_WORKSPACE;
-  const char* base = static_cast<const char*>(workspace);
-  return hip_status(gqa::launch_decode_merge(reinterpret_cast<const float*>(base + ws.o_offset),
-                                             reinterpret_cast<const float*>(base + ws.lse_offset),
-                                             seq_lens, out, s, static_cast<hipStream_t>(stream)));
+  return hip_status(gqa::launch_decode_merge(seq_lens, out, static_cast<const char*>(workspace), s,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -177,12 +175,10 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (st != GQA_OK) return st;
   if (!aligned(out, 16)) return GQA_ERR_ALIGN;
   char* base = static_cast<char*>(workspace);
-  float* po = reinterpret_cast<float*>(base + ws.o_offset);
-  float* pl = reinterpret_cast<float*>(base + ws.lse_offset);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, po, pl, s, hs));
+  st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, out, base, s, hs));
   if (st != GQA_OK) return st;
-  return hip_status(gqa::launch_decode_merge(po, pl, seq_lens, out, s, hs));
+  return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
 }
 
 int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out, float* lse,

@@ -5,26 +5,37 @@
 // (deepconcepts.dev, "Grouped-Query Attention", section "Three numbers that
 // people expect to move together"), far below the MI355X ridge point.  The
 // design therefore reads every K/V element exactly once per group: a
-// workgroup owns one (sequence, KV head, token chunk) and computes all g <= 16
-// query heads of the group against each K/V row it loads (anrans.github.io,
-// "Attention variants: MQA, GQA, MLA", section "Kernels do not need to copy
-// the KV heads": the group's query heads act as extra query rows).
+// workgroup attends a run of tokens of one KV head for all g <= 16 query
+// heads of the group at once (anrans.github.io, "Attention variants: MQA,
+// GQA, MLA", section "Kernels do not need to copy the KV heads": the group's
+// query heads act as extra query rows against the shared K/V).
 //
-// bf16 path (one wavefront = 32 tokens per iteration):
+// Work partition (balanced "stream" split).  A unit is one (sequence, KV
+// head, block of 16 query heads); its work is the sequence's T_b cached
+// tokens.  The units' tokens are laid end to end into one stream of W
+// token-units, and range r of the stream is [r*Q, (r+1)*Q): every range has
+// the same size no matter how ragged the lengths are, and about one range
+// runs per resident workgroup, so no workgroup idles at the tail.  Q is
+// chosen on the device from the actual lengths (Q = ceil(W / workgroups),
+// at least kMinRange) unless the caller fixes it.  The piece of a range that
+// falls inside one unit is a segment; a unit split over n > 1 segments gets
+// n partial results (normalised O and log2-sum-exp) that decode_merge
+// combines, and a unit covered by a single segment is written straight to
+// the output.
+//
+// bf16 path, per wavefront and 32-token tile:
 //   S^T[32 tok, 16 heads] = K[32, d] Q^T[d, 16]      v_mfma_f32_16x16x32_bf16
 //   online softmax per head (column) with wavefront shuffles, log2 domain
 //   O^T[d, 16 heads]    += V^T[d, 32] P^T[32, 16]    (V^T via ds_read_b64_tr_b16)
-// K goes straight from HBM into MFMA operand registers (16-byte loads of 64
-// contiguous bytes per row); V goes through a per-wave LDS tile because the
-// PV contraction runs over tokens, which are strided in memory.
+// K goes straight from HBM into MFMA operand registers (16-byte non-temporal
+// buffer loads, 64 contiguous bytes per row); V goes through a per-wave LDS
+// tile because the PV contraction runs over tokens, which are strided in
+// memory.  The four wavefronts of a workgroup take interleaved tiles of a
+// segment and are combined through LDS at the segment's end.
 //
 // fp32 path: a plain VALU kernel (no fp32 matrix-core shape is worth it at
-// d <= 128), K/V tiles staged once per workgroup in LDS, one query head per
-// wavefront pass.
-//
-// Both write per-chunk partials (O_c normalised, lse_c in log2 units) to the
-// workspace; decode_merge combines them by log-sum-exp.  Chunk c of sequence b
-// covers tokens [c*chunk, min((c+1)*chunk, T_b)); empty chunks exit at once.
+// d <= 128) with the same partition, K/V tiles staged once per workgroup in
+// LDS, one query head per wavefront pass.
 
 #include "gqa_device.hpp"
 #include "gqa_launch.hpp"
@@ -33,9 +44,143 @@ namespace gqa {
 
 namespace {
 
+constexpr int kThreads = kDecodeWaves * 64;
+
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int tcap) {
   int t = lens[b];
   return t < 0 ? 0 : (t > tcap ? tcap : t);
+}
+
+// Segments of a unit occupying stream positions [s, s + t).
+__device__ __forceinline__ int unit_segments(long long s, int t, long long q) {
+  return t == 0 ? 0 : (int)((s + t - 1) / q - s / q + 1);
+}
+
+// A unit of the stream: sequence b, unit j within the sequence (kvh * nhb +
+// head block), its length t, first stream position s and first slot base.
+struct Unit {
+  int b, j, t, base;
+  long long s;
+};
+
+// Stream geometry shared by every workgroup of a launch.
+struct Stream {
+  long long w;        // total token-units
+  long long q;        // tokens per range
+  long long ranges;   // number of ranges
+};
+
+// Every workgroup scans the lengths (two block-wide scans over the batch)
+// so that any stream position maps to its unit and partial-slot index.
+struct ScanSmem {
+  long long tok[kThreads];   // per-thread token base
+  int seg[kThreads];         // per-thread segment base
+  Unit found;
+};
+
+// Block-wide exclusive scan of one value per thread; returns the total.
+template <typename T>
+__device__ T block_exclusive_scan(T* buf, T v) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const T add = tid >= off ? buf[tid - off] : T(0);
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const T total = buf[kThreads - 1];
+  const T excl = buf[tid] - v;
+  __syncthreads();
+  buf[tid] = excl;
+  __syncthreads();
+  return total;
+}
+
+// Thread t owns sequences [t*per, min(B, (t+1)*per)).
+__device__ __forceinline__ void seq_block(int batch, int& b0, int& b1) {
+  const int per = (batch + kThreads - 1) / kThreads;
+  b0 = min(batch, (int)threadIdx.x * per);
+  b1 = min(batch, b0 + per);
+}
+
+__device__ Stream stream_setup(ScanSmem& sm, const int32_t* lens, int batch, int upb, int tcap,
+                               int q_fixed) {
+  int b0, b1;
+  seq_block(batch, b0, b1);
+  long long mine = 0;
+  for (int b = b0; b < b1; ++b) mine += (long long)clamp_len(lens, b, tcap) * upb;
+  Stream st;
+  st.w = block_exclusive_scan(sm.tok, mine);
+  if (q_fixed > 0) {
+    st.q = q_fixed;
+  } else {
+    st.q = (st.w + gridDim.x - 1) / gridDim.x;
+    if (st.q < kMinRange) st.q = kMinRange;
+  }
+  st.ranges = (st.w + st.q - 1) / st.q;
+  // segment counts, now that every unit's first position is known
+  long long s = sm.tok[threadIdx.x];
+  int segs = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int t = clamp_len(lens, b, tcap);
+    for (int j = 0; j < upb; ++j, s += t) segs += unit_segments(s, t, st.q);
+  }
+  block_exclusive_scan(sm.seg, segs);
+  return st;
+}
+
+// The non-empty unit holding stream position x (0 <= x < w).
+__device__ Unit stream_locate(ScanSmem& sm, const int32_t* lens, int batch, int upb, int tcap,
+                              const Stream& st, long long x) {
+  int b0, b1;
+  seq_block(batch, b0, b1);
+  long long s = sm.tok[threadIdx.x];
+  int base = sm.seg[threadIdx.x];
+  for (int b = b0; b < b1; ++b) {
+    const int t = clamp_len(lens, b, tcap);
+    if (t > 0 && x >= s && x < s + (long long)t * upb) {   // x lies in sequence b
+      const int j = (int)((x - s) / t);
+      for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * t, t, st.q);
+      sm.found = Unit{b, j, t, base, s + (long long)j * t};
+      break;
+    }
+    for (int jj = 0; jj < upb; ++jj) base += unit_segments(s + (long long)jj * t, t, st.q);
+    s += (long long)t * upb;
+  }
+  __syncthreads();
+  const Unit u = sm.found;
+  __syncthreads();
+  return u;
+}
+
+// The next non-empty unit after u (the caller knows one exists).
+__device__ __forceinline__ Unit stream_next(const Unit& u, const int32_t* lens, int upb, int tcap,
+                                            long long q) {
+  Unit n = u;
+  n.base = u.base + unit_segments(u.s, u.t, q);
+  n.s = u.s + u.t;
+  if (u.j + 1 < upb) {
+    n.j = u.j + 1;
+    return n;
+  }
+  n.j = 0;
+  n.b = u.b + 1;
+  n.t = clamp_len(lens, n.b, tcap);
+  while (n.t == 0) n.t = clamp_len(lens, ++n.b, tcap);
+  return n;
+}
+
+// Records where the merge finds a unit's partials (written by the
+// workgroup that holds the unit's first segment).
+__device__ __forceinline__ void publish_unit(int* unit_info, const Unit& u, int upb, int nseg,
+                                             int kseg) {
+  if (kseg == 0 && threadIdx.x == 0) {
+    const size_t i = (size_t)u.b * upb + u.j;
+    unit_info[2 * i] = u.base;
+    unit_info[2 * i + 1] = nseg;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -50,157 +195,197 @@ struct DecodeBf16Smem {
   static constexpr int kBytes = kVTile > kComb ? kVTile : kComb;
 };
 
+// One wavefront's 32-token tile in registers: K as MFMA A operands and the
+// V rows as loaded (destined for the wave's LDS tile).
 template <int D>
-__global__ __launch_bounds__(kDecodeWaves * 64)
+struct DecodeTile {
+  bf16x8 k[2][D / 32];
+  bf16x8 v[kDecodeWaveTile * D / 8 / 64];
+};
+
+// Byte offsets are relative to the segment start; rows at or past the
+// segment end lie outside the buffer resource and load as zeros.  The whole
+// offset goes in the per-lane operand: the uniform (SGPR) offset of a buffer
+// access is not covered by the range check.
+template <int D>
+__device__ __forceinline__ void load_tile(DecodeTile<D>& t, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, int k_off, int v_off,
+                                          int tile_bytes) {
+  constexpr int ROW = D * 2;
+  constexpr int RPI = 512 / D;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      t.k[bi][kk] = buffer_load_bf16x8<kCacheStream>(rk, tile_bytes + k_off + bi * 16 * ROW + 64 * kk, 0);
+#pragma unroll
+  for (int i = 0; i < kDecodeWaveTile * D / 8 / 64; ++i)
+    t.v[i] = buffer_load_bf16x8<kCacheStream>(rv, tile_bytes + v_off + i * RPI * ROW, 0);
+}
+
+#ifndef GQA_DECODE_WAVES_PER_EU
+#define GQA_DECODE_WAVES_PER_EU 3
+#endif
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA_DECODE_WAVES_PER_EU)))
 void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                        const __bf16* __restrict__ vc, const int32_t* __restrict__ lens,
-                       float* __restrict__ part_o, float* __restrict__ part_lse,
-                       int hq, int hkv, int g, int nhb, int tcap, int chunk, int nsplit,
-                       float scale_log2) {
+                       float* __restrict__ out, float* __restrict__ part_o,
+                       float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
+                       int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2) {
   constexpr int KSTEPS = D / 32;          // QK^T MFMA steps over the head dim
   constexpr int DBLK = D / 16;            // PV MFMA blocks over the head dim
   constexpr int PITCH = DecodeBf16Smem<D>::kPitch;
   constexpr int LPR = D / 8;              // lanes per V row (16 B each)
   constexpr int RPI = 64 / LPR;           // V rows per wave load
   constexpr int VLOADS = kDecodeWaveTile / RPI;
+  constexpr int STRIDE = kDecodeWaves * kDecodeWaveTile;   // tokens between a wave's tiles
+  constexpr int OP = D + 4;
   __shared__ __align__(16) char smem[DecodeBf16Smem<D>::kBytes];
+  __shared__ ScanSmem scan;
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / nhb;
-  const int hb = blockIdx.y - kvh * nhb;
-  const int b = blockIdx.z;
-  const int T = clamp_len(lens, b, tcap);
-  const int t_begin = split * chunk;
-  if (t_begin >= T) return;
-  const int t_end = min(t_begin + chunk, T);
+  const int upb = hkv * nhb;
+  const Stream st = stream_setup(scan, lens, batch, upb, tcap, q_fixed);
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;   // token row of A / head column of B and D
   const int j = lane >> 4;   // contraction group
-  const int h_first = kvh * g + hb * kDecodeHeadBlock;
-  const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
-
-  // Q^T as the B operand: lane holds q[h_first+n][8j + 32kk .. +7].
-  bf16x8 qb[KSTEPS];
-  {
-    const __bf16* qrow = q + ((size_t)b * hq + h_first + min(n, nh - 1)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      qb[kk] = load_bf16x8(qrow + 8 * j + 32 * kk);
-      if (n >= nh) qb[kk] = bf16x8{};
-    }
-  }
-
-  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)tcap * D;
-  const __bf16* kbase = kc + kv_off;
-  const __bf16* vbase = vc + kv_off;
+  const int k_off = n * D * 2 + 16 * j;                       // + 16*bi rows, + 64*kk bytes
+  const int v_off = (lane / LPR) * D * 2 + 16 * (lane % LPR);  // + RPI*i rows
   __bf16* vt = reinterpret_cast<__bf16*>(smem) + w * kDecodeWaveTile * PITCH;
-
-  float m = -INFINITY;   // running max of head n (log2 domain), same in all 4 lane groups
-  float lsum = 0.f;      // this lane's share of the running denominator of head n
-  f32x4 acc[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int t0 = t_begin + w * kDecodeWaveTile; t0 < t_end; t0 += kDecodeWaves * kDecodeWaveTile) {
-    // K rows t0 + 16*bi + n as A operands; rows past the end re-read the
-    // last valid row (its scores are masked), never the padding.
-    bf16x8 ka[2][KSTEPS];
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const int t = min(t0 + 16 * bi + n, t_end - 1);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) ka[bi][kk] = load_bf16x8(kbase + (size_t)t * D + 8 * j + 32 * kk);
-    }
-    bf16x8 vr[VLOADS];
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int t = min(t0 + i * RPI + lane / LPR, t_end - 1);
-      vr[i] = load_bf16x8(vbase + (size_t)t * D + 8 * (lane % LPR));
-    }
-
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      sc[0] = mfma16(ka[0][kk], qb[kk], sc[0]);
-      sc[1] = mfma16(ka[1][kk], qb[kk], sc[1]);
-    }
-    // sc[bi][r] = score of token t0 + 16*bi + 4*j + r for head n.
-    float s2[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + 16 * (e >> 2) + 4 * j + (e & 3);
-      s2[e] = t < t_end ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s2[e]);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);       // finite: every tile holds a valid token
-    const float alpha = fast_exp2(m - m_new);
-    bf16x8 pb;
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 p = (__bf16)fast_exp2(s2[e] - m_new);
-      pb[e] = p;
-      ps += (float)p;   // the denominator sums exactly the weights PV uses
-    }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) acc[i] *= alpha;
-
-    wave_sync();   // previous iteration's transposed reads are done
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i)
-      store_bf16x8(vt + (i * RPI + lane / LPR) * PITCH + 8 * (lane % LPR), vr[i]);
-    wave_sync();
-    // V^T as the A operand: k-slots 0..3 are tokens 4j..4j+3 and slots 4..7
-    // are tokens 16+4j..16+4j+3, matching the P^T slots in pb.
-    const int L = lane & 15;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const __bf16* base = vt + (4 * j + (L >> 2)) * PITCH + 16 * db + 4 * (L & 3);
-      const bf16x8 va = concat(lds_read_tr16(base), lds_read_tr16(base + 16 * PITCH));
-      acc[db] = mfma16(va, pb, acc[db]);
-    }
-  }
-
-  // Combine the four wavefronts' partial softmax states through LDS.
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
-  __syncthreads();
   float* cm = reinterpret_cast<float*>(smem);
   float* cl = cm + kDecodeWaves * kDecodeHeadBlock;
   float* co = cl + kDecodeWaves * kDecodeHeadBlock;
-  constexpr int OP = D + 4;
-  if (j == 0) {
-    cm[w * kDecodeHeadBlock + n] = m;
-    cl[w * kDecodeHeadBlock + n] = lsum;
-  }
+
+  for (long long r = blockIdx.x; r < st.ranges; r += gridDim.x) {
+    long long lo = r * st.q;
+    const long long hi = min(lo + st.q, st.w);
+    Unit u = stream_locate(scan, lens, batch, upb, tcap, st, lo);
+    while (true) {
+      const int t0 = (int)(lo - u.s);                      // first token of the segment
+      const int nt = (int)(min(hi, u.s + u.t) - lo);       // tokens in the segment
+      const int kvh = u.j / nhb;
+      const int hb = u.j - kvh * nhb;
+      const int h_first = kvh * g + hb * kDecodeHeadBlock;
+      const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
+
+      // Q^T as the B operand: lane holds q[h_first+n][8j + 32kk .. +7].
+      bf16x8 qb[KSTEPS];
+      {
+        const __bf16* qrow = q + ((size_t)u.b * hq + h_first + min(n, nh - 1)) * D;
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          qb[kk] = load_bf16x8(qrow + 8 * j + 32 * kk);
+          if (n >= nh) qb[kk] = bf16x8{};
+        }
+      }
+      const size_t seg_off = (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + seg_off, nt * D * 2);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + seg_off, nt * D * 2);
+
+      float m = -INFINITY;   // running max of head n (log2 domain), same in all 4 lane groups
+      float lsum = 0.f;      // this lane's share of the running denominator of head n
+      f32x4 acc[DBLK];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) co[(w * kDecodeHeadBlock + n) * OP + 16 * db + 4 * j + r] = acc[db][r];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * D; idx += kDecodeWaves * 64) {
-    const int h = idx / D;
-    const int dd = idx - h * D;
-    float M = -INFINITY;
+      for (int i = 0; i < DBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      for (int tok = w * kDecodeWaveTile; tok < nt; tok += STRIDE) {
+        DecodeTile<D> tl;
+        load_tile<D>(tl, rk, rv, k_off, v_off, tok * D * 2);
+        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ww = 0; ww < kDecodeWaves; ++ww) M = fmaxf(M, cm[ww * kDecodeHeadBlock + h]);
-    float Ls = 0.f, Os = 0.f;
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          sc[0] = mfma16(tl.k[0][kk], qb[kk], sc[0]);
+          sc[1] = mfma16(tl.k[1][kk], qb[kk], sc[1]);
+        }
+        // sc[bi][r] = score of token tok + 16*bi + 4*j + r for head n.
+        float s2[8];
+        float mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kDecodeWaves; ++ww) {
-      const float wt = fast_exp2(cm[ww * kDecodeHeadBlock + h] - M);   // 0 for idle waves
-      Ls += cl[ww * kDecodeHeadBlock + h] * wt;
-      Os += co[(ww * kDecodeHeadBlock + h) * OP + dd] * wt;
+        for (int e = 0; e < 8; ++e) {
+          const int tt = tok + 16 * (e >> 2) + 4 * j + (e & 3);
+          s2[e] = tt < nt ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s2[e]);
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);       // finite: every tile holds a valid token
+        const float alpha = fast_exp2(m - m_new);
+        bf16x8 pb;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 p = (__bf16)fast_exp2(s2[e] - m_new);
+          pb[e] = p;
+          ps += (float)p;   // the denominator sums exactly the weights PV uses
+        }
+        lsum = lsum * alpha + ps;
+        m = m_new;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) acc[i] *= alpha;
+
+        wave_sync();   // the previous tile's transposed reads are done
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i)
+          store_bf16x8(vt + (i * RPI + lane / LPR) * PITCH + 8 * (lane % LPR), tl.v[i]);
+        wave_sync();
+        // V^T as the A operand: k-slots 0..3 are tokens 4j..4j+3 and slots
+        // 4..7 are tokens 16+4j..16+4j+3, matching the P^T slots in pb.
+        const int L = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const __bf16* base = vt + (4 * j + (L >> 2)) * PITCH + 16 * db + 4 * (L & 3);
+          const bf16x8 va = concat(lds_read_tr16(base), lds_read_tr16(base + 16 * PITCH));
+          acc[db] = mfma16(va, pb, acc[db]);
+        }
+      }
+
+      // Combine the four wavefronts' softmax states through LDS.
+      lsum += shfl_xor(lsum, 16);
+      lsum += shfl_xor(lsum, 32);
+      __syncthreads();   // every wave is done with its V tile
+      if (j == 0) {
+        cm[w * kDecodeHeadBlock + n] = m;
+        cl[w * kDecodeHeadBlock + n] = lsum;
+      }
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          co[(w * kDecodeHeadBlock + n) * OP + 16 * db + 4 * j + rr] = acc[db][rr];
+      __syncthreads();
+      const int nseg = unit_segments(u.s, u.t, st.q);
+      const int kseg = (int)(r - u.s / st.q);
+      const size_t slot = (size_t)u.base + kseg;
+      for (int idx = threadIdx.x; idx < nh * D; idx += kThreads) {
+        const int h = idx / D;
+        const int dd = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kDecodeWaves; ++ww) M = fmaxf(M, cm[ww * kDecodeHeadBlock + h]);
+        float Ls = 0.f, Os = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDecodeWaves; ++ww) {
+          const float wt = fast_exp2(cm[ww * kDecodeHeadBlock + h] - M);   // 0 for idle waves
+          Ls += cl[ww * kDecodeHeadBlock + h] * wt;
+          Os += co[(ww * kDecodeHeadBlock + h) * OP + dd] * wt;
+        }
+        if (nseg == 1) {
+          out[((size_t)u.b * hq + h_first + h) * D + dd] = Os / Ls;
+        } else {
+          part_o[(slot * kDecodeHeadBlock + h) * D + dd] = Os / Ls;
+          if (dd == 0) part_lse[slot * kDecodeHeadBlock + h] = M + __log2f(Ls);
+        }
+      }
+      publish_unit(unit_info, u, upb, nseg, kseg);
+      lo += nt;
+      if (lo >= hi) break;
+      __syncthreads();   // the combine buffers are read before the next segment's tiles
+      u = stream_next(u, lens, upb, tcap, st.q);
     }
-    const size_t row = ((size_t)b * hq + h_first + h) * nsplit + split;
-    part_o[row * D + dd] = Os / Ls;
-    if (dd == 0) part_lse[row] = M + __log2f(Ls);
+    __syncthreads();
   }
 }
 
@@ -211,170 +396,247 @@ constexpr int kF32Tile = 64;        // tokens per workgroup iteration
 constexpr int kF32HeadsPerWave = kDecodeHeadBlock / kDecodeWaves;
 
 template <int D>
-__global__ __launch_bounds__(kDecodeWaves * 64)
+__global__ __launch_bounds__(kThreads)
 void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
                       const float* __restrict__ vc, const int32_t* __restrict__ lens,
-                      float* __restrict__ part_o, float* __restrict__ part_lse,
-                      int hq, int hkv, int g, int nhb, int tcap, int chunk, int nsplit,
-                      float scale_log2) {
+                      float* __restrict__ out, float* __restrict__ part_o,
+                      float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
+                      int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2) {
   constexpr int P = D + 1;          // odd pitch: column reads are conflict-free
   constexpr int CPL = D / 64;       // output columns per lane
   __shared__ float ks[kF32Tile * P];
   __shared__ float vs[kF32Tile * P];
   __shared__ float qs[kDecodeHeadBlock * D];
   __shared__ float pw[kDecodeWaves][kF32Tile];
+  __shared__ ScanSmem scan;
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / nhb;
-  const int hb = blockIdx.y - kvh * nhb;
-  const int b = blockIdx.z;
-  const int T = clamp_len(lens, b, tcap);
-  const int t_begin = split * chunk;
-  if (t_begin >= T) return;
-  const int t_end = min(t_begin + chunk, T);
+  const int upb = hkv * nhb;
+  const Stream st = stream_setup(scan, lens, batch, upb, tcap, q_fixed);
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int h_first = kvh * g + hb * kDecodeHeadBlock;
-  const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
 
-  for (int i = threadIdx.x; i < nh * D; i += blockDim.x)
-    qs[i] = q[((size_t)b * hq + h_first) * D + i];
+  for (long long r = blockIdx.x; r < st.ranges; r += gridDim.x) {
+    long long lo = r * st.q;
+    const long long hi = min(lo + st.q, st.w);
+    Unit u = stream_locate(scan, lens, batch, upb, tcap, st, lo);
+    while (true) {
+      const int t0 = (int)(lo - u.s);
+      const int nt = (int)(min(hi, u.s + u.t) - lo);
+      const int kvh = u.j / nhb;
+      const int hb = u.j - kvh * nhb;
+      const int h_first = kvh * g + hb * kDecodeHeadBlock;
+      const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
 
-  float m[kF32HeadsPerWave], l[kF32HeadsPerWave], o[kF32HeadsPerWave][CPL];
-#pragma unroll
-  for (int s = 0; s < kF32HeadsPerWave; ++s) {
-    m[s] = -INFINITY;
-    l[s] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[s][c] = 0.f;
-  }
-  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)tcap * D;
+      for (int i = threadIdx.x; i < nh * D; i += kThreads)
+        qs[i] = q[((size_t)u.b * hq + h_first) * D + i];
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kF32Tile) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kF32Tile * D; i += blockDim.x) {
-      const int r = i / D, c = i - (i / D) * D;
-      const int t = min(t0 + r, t_end - 1);
-      ks[r * P + c] = kc[kv_off + (size_t)t * D + c];
-      vs[r * P + c] = vc[kv_off + (size_t)t * D + c];
-    }
-    __syncthreads();
-    const bool valid = t0 + lane < t_end;
-#pragma unroll 1
-    for (int s = 0; s < kF32HeadsPerWave; ++s) {
-      const int hl = w + kDecodeWaves * s;
-      if (hl >= nh) break;
-      float dot = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < D; ++c) dot = fmaf(qs[hl * D + c], ks[lane * P + c], dot);
-      const float s2 = valid ? dot * scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m[s], wave_max(s2));
-      const float alpha = fast_exp2(m[s] - m_new);
-      const float p = fast_exp2(s2 - m_new);
-      l[s] = l[s] * alpha + wave_sum(p);
-      m[s] = m_new;
-      pw[w][lane] = p;
-      wave_sync();
+      float m[kF32HeadsPerWave], l[kF32HeadsPerWave], o[kF32HeadsPerWave][CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float acc = o[s][c] * alpha;
-#pragma unroll 8
-        for (int t = 0; t < kF32Tile; ++t) acc = fmaf(pw[w][t], vs[t * P + lane + 64 * c], acc);
-        o[s][c] = acc;
+      for (int s = 0; s < kF32HeadsPerWave; ++s) {
+        m[s] = -INFINITY;
+        l[s] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[s][c] = 0.f;
       }
-      wave_sync();
+      const size_t kv_off = (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D;
+
+      for (int tt0 = 0; tt0 < nt; tt0 += kF32Tile) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < kF32Tile * D; i += kThreads) {
+          const int rr = i / D, c = i - (i / D) * D;
+          const int t = min(tt0 + rr, nt - 1);   // rows past the end repeat the last valid row
+          ks[rr * P + c] = kc[kv_off + (size_t)t * D + c];
+          vs[rr * P + c] = vc[kv_off + (size_t)t * D + c];
+        }
+        __syncthreads();
+        const bool valid = tt0 + lane < nt;
+#pragma unroll 1
+        for (int s = 0; s < kF32HeadsPerWave; ++s) {
+          const int hl = w + kDecodeWaves * s;
+          if (hl >= nh) break;
+          float dot = 0.f;
+#pragma unroll 8
+          for (int c = 0; c < D; ++c) dot = fmaf(qs[hl * D + c], ks[lane * P + c], dot);
+          const float s2 = valid ? dot * scale_log2 : -INFINITY;
+          const float m_new = fmaxf(m[s], wave_max(s2));
+          const float alpha = fast_exp2(m[s] - m_new);
+          const float p = fast_exp2(s2 - m_new);
+          l[s] = l[s] * alpha + wave_sum(p);
+          m[s] = m_new;
+          pw[w][lane] = p;
+          wave_sync();
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            float a = o[s][c] * alpha;
+#pragma unroll 8
+            for (int t = 0; t < kF32Tile; ++t) a = fmaf(pw[w][t], vs[t * P + lane + 64 * c], a);
+            o[s][c] = a;
+          }
+          wave_sync();
+        }
+      }
+      const int nseg = unit_segments(u.s, u.t, st.q);
+      const int kseg = (int)(r - u.s / st.q);
+      const size_t slot = (size_t)u.base + kseg;
+#pragma unroll
+      for (int s = 0; s < kF32HeadsPerWave; ++s) {
+        const int hl = w + kDecodeWaves * s;
+        if (hl >= nh) break;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float val = o[s][c] / l[s];
+          if (nseg == 1)
+            out[((size_t)u.b * hq + h_first + hl) * D + lane + 64 * c] = val;
+          else
+            part_o[(slot * kDecodeHeadBlock + hl) * D + lane + 64 * c] = val;
+        }
+        if (nseg != 1 && lane == 0) part_lse[slot * kDecodeHeadBlock + hl] = m[s] + __log2f(l[s]);
+      }
+      publish_unit(unit_info, u, upb, nseg, kseg);
+      lo += nt;
+      if (lo >= hi) break;
+      u = stream_next(u, lens, upb, tcap, st.q);
+      __syncthreads();   // qs is rewritten for the next unit
     }
-  }
-#pragma unroll
-  for (int s = 0; s < kF32HeadsPerWave; ++s) {
-    const int hl = w + kDecodeWaves * s;
-    if (hl >= nh) break;
-    const size_t row = ((size_t)b * hq + h_first + hl) * nsplit + split;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) part_o[row * D + lane + 64 * c] = o[s][c] / l[s];
-    if (lane == 0) part_lse[row] = m[s] + __log2f(l[s]);
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the chunk partials: one workgroup per (query head,
-// sequence), one thread per head coordinate.
+// Log-sum-exp merge of the segment partials: one workgroup per (query head,
+// sequence).  Threads hold 4 head coordinates each; D/4 threads cover one
+// partial row and the 256 threads walk 1024/D rows at a time, so many loads
+// are in flight; the row groups are then combined through LDS.  Units
+// written directly by a single segment are skipped; empty sequences get
+// zeros.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128)
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads)
 void decode_merge(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                  const int32_t* __restrict__ lens, float* __restrict__ out, int hq, int d,
-                  int tcap, int chunk, int nsplit) {
+                  const int* __restrict__ unit_info, const int32_t* __restrict__ lens,
+                  float* __restrict__ out, int hq, int hkv, int g, int nhb, int tcap) {
+  constexpr int C4 = D / 4;                  // float4 columns per row
+  constexpr int ROWS = kMergeThreads / C4;   // partial rows read concurrently
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4 racc[ROWS][C4];
+  __shared__ float rl[ROWS];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int dd = threadIdx.x;
-  if (dd >= d) return;
-  const int T = clamp_len(lens, b, tcap);
-  const int ns = (T + chunk - 1) / chunk;
-  const size_t row0 = ((size_t)b * hq + h) * nsplit;
-  float* o = out + ((size_t)b * hq + h) * d + dd;
-  if (ns == 0) {   // empty sequence: all-zero output
-    *o = 0.f;
+  const int tid = threadIdx.x;
+  float* o = out + ((size_t)b * hq + h) * D;
+  if (clamp_len(lens, b, tcap) == 0) {   // empty sequence: all-zero output
+    for (int i = tid; i < D; i += kMergeThreads) o[i] = 0.f;
     return;
   }
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_lse[row0 + s]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = fast_exp2(part_lse[row0 + s] - M);
+  const int kvh = h / g;
+  const int hb = (h - kvh * g) / kDecodeHeadBlock;
+  const int hl = (h - kvh * g) - hb * kDecodeHeadBlock;
+  const size_t unit = ((size_t)b * hkv + kvh) * nhb + hb;
+  const int base = unit_info[2 * unit];
+  const int ns = unit_info[2 * unit + 1];
+  if (ns <= 1) return;   // written directly by its only segment
+
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += kMergeThreads)
+    mx = fmaxf(mx, part_lse[((size_t)base + s) * kDecodeHeadBlock + hl]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+
+  const int c4 = tid % C4;
+  const int sr = tid / C4;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = sr; s < ns; s += ROWS) {
+    const size_t row = ((size_t)base + s) * kDecodeHeadBlock + hl;
+    const float wt = fast_exp2(part_lse[row] - M);
     L += wt;
-    acc = fmaf(wt, part_o[(row0 + s) * d + dd], acc);
+    acc += wt * reinterpret_cast<const f32x4*>(part_o + row * D)[c4];
   }
-  *o = acc / L;
+  racc[sr][c4] = acc;
+  if (c4 == 0) rl[sr] = L;
+  __syncthreads();
+  if (sr == 0) {
+    float Lt = rl[0];
+    f32x4 a = racc[0][c4];
+#pragma unroll
+    for (int rr = 1; rr < ROWS; ++rr) {
+      Lt += rl[rr];
+      a += racc[rr][c4];
+    }
+    reinterpret_cast<f32x4*>(o)[c4] = a / Lt;
+  }
 }
 
 }  // namespace
 
 DecodeWorkspace decode_workspace_layout(const DecodeShape& s) {
-  const int64_t rows = (int64_t)s.batch * s.hq * s.nsplit;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   DecodeWorkspace w;
-  w.o_offset = 0;
-  w.lse_offset = ((rows * s.d * 4 + 255) / 256) * 256;
-  w.total = w.lse_offset + ((rows * 4 + 255) / 256) * 256;
+  w.info_offset = 0;
+  w.lse_offset = up((int64_t)s.units * 2 * 4);
+  w.o_offset = w.lse_offset + up(s.max_slots * kDecodeHeadBlock * 4);
+  w.total = w.o_offset + up(s.max_slots * kDecodeHeadBlock * (int64_t)s.d * 4);
   return w;
 }
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
-                               float* part_o, float* part_lse, const DecodeShape& s,
+                               float* out, char* workspace, const DecodeShape& s,
                                hipStream_t stream) {
   const int g = s.hq / s.hkv;
   const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
-  const dim3 grid(s.nsplit, s.hkv * nhb, s.batch);
-  const dim3 block(kDecodeWaves * 64);
+  const DecodeWorkspace wl = decode_workspace_layout(s);
+  int* info = reinterpret_cast<int*>(workspace + wl.info_offset);
+  float* plse = reinterpret_cast<float*>(workspace + wl.lse_offset);
+  float* po = reinterpret_cast<float*>(workspace + wl.o_offset);
+  const dim3 grid(s.grid);
+  const dim3 block(kThreads);
   const float sl2 = s.scale * kLog2e;
   if (s.dtype == 1) {
     auto qp = static_cast<const __bf16*>(q);
     auto kp = static_cast<const __bf16*>(k);
     auto vp = static_cast<const __bf16*>(v);
     if (s.d == 128)
-      hipLaunchKernelGGL(decode_split_bf16<128>, grid, block, 0, stream, qp, kp, vp, lens, part_o,
-                         part_lse, s.hq, s.hkv, g, nhb, s.tcap, s.chunk, s.nsplit, sl2);
+      hipLaunchKernelGGL(decode_split_bf16<128>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
     else
-      hipLaunchKernelGGL(decode_split_bf16<64>, grid, block, 0, stream, qp, kp, vp, lens, part_o,
-                         part_lse, s.hq, s.hkv, g, nhb, s.tcap, s.chunk, s.nsplit, sl2);
+      hipLaunchKernelGGL(decode_split_bf16<64>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
   } else {
     auto qp = static_cast<const float*>(q);
     auto kp = static_cast<const float*>(k);
     auto vp = static_cast<const float*>(v);
     if (s.d == 128)
-      hipLaunchKernelGGL(decode_split_f32<128>, grid, block, 0, stream, qp, kp, vp, lens, part_o,
-                         part_lse, s.hq, s.hkv, g, nhb, s.tcap, s.chunk, s.nsplit, sl2);
+      hipLaunchKernelGGL(decode_split_f32<128>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
     else
-      hipLaunchKernelGGL(decode_split_f32<64>, grid, block, 0, stream, qp, kp, vp, lens, part_o,
-                         part_lse, s.hq, s.hkv, g, nhb, s.tcap, s.chunk, s.nsplit, sl2);
+      hipLaunchKernelGGL(decode_split_f32<64>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(const float* part_o, const float* part_lse, const int32_t* lens,
-                               float* out, const DecodeShape& s, hipStream_t stream) {
+hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
+                               const DecodeShape& s, hipStream_t stream) {
+  const int g = s.hq / s.hkv;
+  const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
+  const DecodeWorkspace wl = decode_workspace_layout(s);
+  const int* info = reinterpret_cast<const int*>(workspace + wl.info_offset);
+  const float* plse = reinterpret_cast<const float*>(workspace + wl.lse_offset);
+  const float* po = reinterpret_cast<const float*>(workspace + wl.o_offset);
   const dim3 grid(s.hq, s.batch);
-  hipLaunchKernelGGL(decode_merge, grid, dim3(128), 0, stream, part_o, part_lse, lens, out, s.hq,
-                     s.d, s.tcap, s.chunk, s.nsplit);
+  if (s.d == 128)
+    hipLaunchKernelGGL(decode_merge<128>, grid, dim3(kMergeThreads), 0, stream, po, plse, info, lens,
+                       out, s.hq, s.hkv, g, nhb, s.tcap);
+  else
+    hipLaunchKernelGGL(decode_merge<64>, grid, dim3(kMergeThreads), 0, stream, po, plse, info, lens,
+                       out, s.hq, s.hkv, g, nhb, s.tcap);
   return hipGetLastError();
 }
 

@@ -74,6 +74,27 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Raw buffer resource over [base, base + bytes): loads whose per-lane byte
+// offset (plus the instruction's immediate offset) is past `bytes` return
+// zeros instead of touching memory; the uniform SGPR offset is NOT range
+// checked, so callers keep it 0.  Dword 3 selects the 32-bit data format
+// that untyped gfx9 buffer loads require.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Cache-policy bits of buffer loads: 2 marks the access non-temporal (nt),
+// for data read exactly once, such as a decode step's sweep of the KV cache.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+
+// 16-byte buffer load at byte offset voff (per lane) + soff (uniform).
+template <int kPolicy = kCacheDefault>
+__device__ __forceinline__ bf16x8 buffer_load_bf16x8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kPolicy));
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

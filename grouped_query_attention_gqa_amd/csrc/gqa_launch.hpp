@@ -12,30 +12,41 @@ constexpr int kDecodeHeadBlock = 16;
 // Decode: tokens per wavefront iteration (bf16 path) and waves per workgroup.
 constexpr int kDecodeWaveTile = 32;
 constexpr int kDecodeWaves = 4;
-// Split sizes are multiples of this many tokens.
-constexpr int kSplitQuantum = 64;
+// Caller-fixed range sizes are positive multiples of this many tokens.
+constexpr int kRangeQuantum = 32;
+// Smallest automatic range: below this, per-range overhead dominates.
+constexpr int kMinRange = 256;
+// Persistent decode workgroups: 256 CUs x 2 resident 4-wave workgroups.
+#ifndef GQA_DECODE_GRID
+#define GQA_DECODE_GRID 512
+#endif
+constexpr int kPersistentWorkgroups = GQA_DECODE_GRID;
 
 struct DecodeShape {
   int batch, hq, hkv, d, tcap;
-  int chunk;   // tokens per split
-  int nsplit;  // split slots per sequence = ceil(tcap / chunk)
+  int units;         // batch * hkv * ceil(g / 16)
+  int q_fixed;       // tokens per range fixed by the caller, 0 = chosen on the device
+  int grid;          // workgroups launched
+  int64_t max_slots; // upper bound on partial slots (ranges + units)
   float scale;
-  int dtype;   // gqa_dtype
+  int dtype;         // gqa_dtype
 };
 
-// Byte offsets of the two workspace arrays.
+// Byte offsets of the workspace arrays: per-unit (first slot, segment
+// count), then per-slot log2-sum-exp [slots][16], then per-slot normalised
+// outputs [slots][16][d], each 256-byte aligned.
 struct DecodeWorkspace {
-  int64_t o_offset, lse_offset, total;
+  int64_t info_offset, lse_offset, o_offset, total;
 };
 
 DecodeWorkspace decode_workspace_layout(const DecodeShape& s);
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
-                               float* part_o, float* part_lse, const DecodeShape& s,
+                               float* out, char* workspace, const DecodeShape& s,
                                hipStream_t stream);
 
-hipError_t launch_decode_merge(const float* part_o, const float* part_lse, const int32_t* lens,
-                               float* out, const DecodeShape& s, hipStream_t stream);
+hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
+                               const DecodeShape& s, hipStream_t stream);
 
 struct PrefillShape {
   int batch, hq, hkv, n, d;

@@ -51,7 +51,7 @@ typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
   GQA_ERR_SHAPE = 2,       /* size < 1, Hkv not dividing Hq, or size overflow    */
-  GQA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype not allowed, bad split  */
+  GQA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype not allowed, bad range  */
   GQA_ERR_WORKSPACE = 4,   /* workspace smaller than gqa_decode_plan requires    */
   GQA_ERR_HIP = 5,         /* the HIP runtime rejected a launch                  */
   GQA_ERR_ALIGN = 6        /* a pointer violates the alignment rule above        */
@@ -72,23 +72,26 @@ const char* gqa_status_string(int32_t status);
 const char* gqa_last_hip_error(void);
 
 /*
- * Split plan of a decode call.  Decode cuts every sequence's cached tokens
- * into chunks of *chunk_tokens_out tokens (the last one ragged); one
- * workgroup attends one chunk for one KV head and all query heads of its
- * group, and the chunk results are merged by log-sum-exp.  This split is an
+ * Launch plan of a decode call.  Decode lays the cached tokens of every
+ * (sequence, KV head, block of up to 16 query heads) end to end into one
+ * stream and cuts it into equal ranges, one per workgroup, so ragged batches
+ * stay balanced; a range's piece inside one sequence is attended by one
+ * workgroup for all query heads of the group, and a sequence that spans
+ * several pieces is finished by a log-sum-exp merge.  This partition is an
  * implementation choice, not something the pages specify.
  *
- * split_tokens: 0 chooses the chunk automatically from the shape; otherwise
- *   a positive multiple of 64 (GQA_ERR_UNSUPPORTED if not).
- * Outputs (any may be NULL): chunk size in tokens, number of chunk slots per
- *   sequence (ceil(max_seq_len / chunk)), and the workspace bytes that
+ * split_tokens: 0 lets the device size the ranges from the actual lengths
+ *   (about one range per resident workgroup); otherwise a positive multiple
+ *   of 32 that fixes the range size (GQA_ERR_UNSUPPORTED if not).
+ * Outputs (any may be NULL): the fixed range size (0 when chosen on the
+ *   device), the number of workgroups launched, and the workspace bytes that
  *   gqa_decode / gqa_decode_split / gqa_decode_merge need for this shape.
  * Pure host arithmetic: never touches the GPU.
  */
 int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_seq_len, int32_t dtype,
-                        int32_t split_tokens, int32_t* chunk_tokens_out,
-                        int32_t* num_splits_out, int64_t* workspace_bytes_out);
+                        int32_t split_tokens, int32_t* range_tokens_out,
+                        int32_t* workgroups_out, int64_t* workspace_bytes_out);
 
 /*
  * One decode step of GQA over a KV cache: every query head of every sequence
@@ -99,7 +102,7 @@ int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
  *   v_cache   [batch, num_kv_heads, max_seq_len, head_dim]       dtype
  *   seq_lens  [batch] int32, device memory, never read on the host; values
  *             are clamped to [0, max_seq_len]; slots past seq_lens[b] are
- *             never used (they may hold garbage, NaN included).  A length of
+ *             never read (they may hold garbage, NaN included).  A length of
  *             0 gives an all-zero output row.
  *   out       [batch, num_q_heads, head_dim] float32
  *   scale     multiplies q . k (1/sqrt(head_dim) for standard attention)
@@ -108,6 +111,7 @@ int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
  *             (its contents on entry do not matter; they are overwritten)
  *
  * Runs gqa_decode_split then gqa_decode_merge on the same stream.
+ * Limits: max_seq_len * head_dim * 4 < 2^31.
  */
 int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* seq_lens, float* out, int32_t batch,
@@ -117,24 +121,25 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                    void* stream);
 
 /*
- * First stage of gqa_decode: attention of every (sequence, chunk, query
- * head) written as a normalised partial output and its log-sum-exp into the
- * workspace.  Arguments as for gqa_decode, without out.  Exposed so that
- * chunk partials can be produced in one place and merged in another (for
- * example after gathering them from several devices).
+ * First stage of gqa_decode (the kernel that reads the KV cache).  Rows of
+ * out whose sequence falls in a single range are written in final form;
+ * every other (sequence, query head) leaves one normalised partial output
+ * and its log-sum-exp per range in the workspace, with an index of them.
+ * Arguments as for gqa_decode.
  */
 int32_t gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
-                         float scale, int32_t dtype, int32_t split_tokens,
-                         void* workspace, int64_t workspace_bytes, void* stream);
+                         const int32_t* seq_lens, float* out, int32_t batch,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_seq_len, float scale, int32_t dtype,
+                         int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                         void* stream);
 
 /*
- * Second stage of gqa_decode: combine the chunk partials of every (sequence,
- * query head) held in the workspace into out [batch, num_q_heads, head_dim]
- * float32, weighting chunk c by exp(lse_c - max_c lse_c).  The shape
+ * Second stage of gqa_decode: the remaining rows of out [batch, num_q_heads,
+ * head_dim] float32, each the combination of its partials weighted by
+ * exp(lse_c - max_c lse_c), and zeros for empty sequences.  The shape
  * arguments must equal those of the gqa_decode_split call that filled the
- * workspace.
+ * workspace, with no other use of the workspace in between.
  */
 int32_t gqa_decode_merge(const int32_t* seq_lens, float* out, int32_t batch,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

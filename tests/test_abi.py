@@ -48,15 +48,17 @@ def test_version_and_status_strings(lib):
 
 def test_plan_auto_and_explicit():
     p = gqa.gqa_decode_plan(32, 32, 8, 128, 8192, BF16)
-    assert p.chunk_tokens % 256 == 0 and p.num_splits == -(-8192 // p.chunk_tokens)
-    rows = 32 * 32 * p.num_splits
-    assert p.workspace_bytes >= rows * 128 * 4 + rows * 4
+    assert p.range_tokens == 0 and p.workgroups == 512      # persistent grid, range size on device
+    units = 32 * 8
+    slots = p.workgroups + units                            # ranges + one extra piece per unit
+    assert p.workspace_bytes >= units * 8 + slots * 16 * (128 + 1) * 4
     one = gqa.gqa_decode_plan(1, 8, 2, 64, 256, F32)
-    assert one.num_splits == 1 and one.chunk_tokens >= 256
+    assert one.workgroups == 2                              # 2 units x 256 tokens, 256-token minimum
     e = gqa.gqa_decode_plan(2, 4, 1, 64, 1000, BF16, split_tokens=128)
-    assert e.chunk_tokens == 128 and e.num_splits == 8
-    # the MQA long-context shape is cut into many splits to fill the GPU
-    assert gqa.gqa_decode_plan(4, 16, 1, 128, 131072, BF16).num_splits >= 64
+    assert e.range_tokens == 128 and e.workgroups == 16     # ceil(2 * 1000 / 128)
+    # 71 query heads on one KV head: 5 blocks of 16 heads, each its own unit
+    big = gqa.gqa_decode_plan(1, 71, 1, 128, 4096, BF16, split_tokens=4096)
+    assert big.workgroups == 5
 
 
 @pytest.mark.parametrize("args,status", [
@@ -66,7 +68,7 @@ def test_plan_auto_and_explicit():
     ((1, 8, 2, 64, 0, BF16, 0), SHAPE),
     ((1, 8, 2, 96, 256, BF16, 0), UNSUP),      # head_dim
     ((1, 8, 2, 64, 256, 7, 0), UNSUP),         # dtype
-    ((1, 8, 2, 64, 256, BF16, 100), UNSUP),    # split not a multiple of 64
+    ((1, 8, 2, 64, 256, BF16, 100), UNSUP),    # range not a multiple of 32
     ((1, 8, 2, 64, 256, BF16, -64), UNSUP),
 ])
 def test_plan_rejects(lib, args, status):
@@ -95,8 +97,9 @@ def test_decode_validation(lib):
 
 
 def test_split_and_merge_validation(lib):
-    assert lib.gqa_decode_split(FAKE, FAKE, None, FAKE, 1, 8, 2, 64, 256, 0.1, BF16, 0, FAKE, 1 << 30, None) == NULL
-    assert lib.gqa_decode_split(FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 256, 0.1, BF16, 0, FAKE, 8, None) == WS
+    assert lib.gqa_decode_split(FAKE, FAKE, None, FAKE, FAKE, 1, 8, 2, 64, 256, 0.1, BF16, 0, FAKE, 1 << 30, None) == NULL
+    assert lib.gqa_decode_split(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 2, 64, 256, 0.1, BF16, 0, FAKE, 1 << 30, None) == NULL
+    assert lib.gqa_decode_split(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 256, 0.1, BF16, 0, FAKE, 8, None) == WS
     assert lib.gqa_decode_merge(FAKE, None, 1, 8, 2, 64, 256, BF16, 0, FAKE, 1 << 30, None) == NULL
     assert lib.gqa_decode_merge(FAKE, FAKE, 1, 9, 2, 64, 256, BF16, 0, FAKE, 1 << 30, None) == SHAPE
     assert lib.gqa_decode_merge(FAKE, FAKE, 1, 8, 2, 64, 256, BF16, 0, FAKE, 8, None) == WS
