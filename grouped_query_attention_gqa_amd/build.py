@@ -31,7 +31,7 @@ def command(out: str = LIB_PATH):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed-FP32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
+        "-Wall", "-Wno-unused-function", "-Wl,--no-undefined",
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,

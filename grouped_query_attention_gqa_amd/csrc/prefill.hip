@@ -10,17 +10,24 @@
 //
 // Workgroup = 4 wavefronts = 128 query rows of ONE KV head: Gw query heads
 // of the group x Mq = 128/Gw consecutive positions (Gw = 4, 2 or 1, the
-// largest dividing g).  Each K/V tile is loaded into LDS once and used by all
-// Gw heads.  Wavefront w owns 32 rows (one head, 32 positions) and keeps:
+// largest dividing g).  Each 64-key K/V tile is loaded into LDS once and used
+// by all Gw heads.  Wavefront w owns 32 rows (one head, 32 positions) and
+// keeps:
 //   Q^T      as MFMA B operands in registers (loaded once),
-//   S^T      [32 keys, 32 rows] = K Q^T in registers,
+//   S^T      [64 keys, 32 rows] = K Q^T in registers,
 //   O^T      [d, 32 rows] fp32 accumulators, rescaled by the online softmax.
-// K tiles feed the A operand with plain 16-byte LDS reads; V tiles feed the
-// A operand of O^T += V^T P^T through the transposing ds_read_b64_tr_b16.
-// Key tiles strictly above a wavefront's diagonal are skipped, and the mask
-// is applied only where a tile crosses it.  Workgroups are issued
-// heaviest-first and, when the (sequence, KV head) count allows, all
-// q-tiles of one KV head land on the same XCD so its K/V stays in one L2.
+// K/V tiles are double-buffered in LDS and filled by direct global-to-LDS
+// buffer loads (no register staging) while the previous tile is computed;
+// one barrier per tile.  The two stages are separate LDS arrays and the loop
+// is unrolled by two, so the compiler can see that reading one stage does not
+// alias the loads in flight into the other.  Tiles are stored in 16-byte
+// chunks with the chunk index XOR-ed by a rotation of the key index, which
+// keeps both the K reads (ds_read_b128, 16 keys x one chunk per 16 lanes)
+// and the transposing V reads (ds_read_b64_tr_b16, 4 keys x 2 chunks per 16
+// lanes) free of bank conflicts.  Key tiles above a wavefront's diagonal are
+// skipped and the mask is applied only where a tile crosses it.  Workgroups
+// are issued heaviest-first and, when the (sequence, KV head) count allows,
+// all q-tiles of one KV head land on the same XCD so its K/V stays in one L2.
 
 #include "gqa_device.hpp"
 #include "gqa_launch.hpp"
@@ -30,21 +37,181 @@ namespace gqa {
 namespace {
 
 constexpr int kRows = 128;   // query rows per workgroup
-constexpr int kBN = 32;      // keys per tile
+constexpr int kBN = 64;      // keys per tile
 constexpr int kXcds = 8;
+constexpr int kPrefillThreads = 256;
+
+// Physical 16-byte chunk of logical chunk c in key row r: c ^ rot(r), with
+// rot a one-bit left rotation of r within the chunk-index width (a
+// bijection that is linear under XOR).
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int BITS = CPR == 16 ? 4 : 3;
+  const int x = r & (CPR - 1);
+  return c ^ (((x << 1) | (x >> (BITS - 1))) & (CPR - 1));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Start the direct global-to-LDS loads of one K tile and one V tile (keys
+// t0 .. t0+63): the wave's lanes fill consecutive 16-byte chunks of its 1 KiB
+// block per instruction, each from the global offset src_off[i].
+template <int D, int LOADS>
+__device__ __forceinline__ void issue_tile(__bf16* kdst, __bf16* vdst, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, const int (&src_off)[LOADS],
+                                           int w, int t0) {
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int dst = (w * 64 + kPrefillThreads * i) * 8;   // wave's 1 KiB block, in bf16 units
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kdst + dst), 16,
+                                             t0 * D * 2 + src_off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vdst + dst), 16,
+                                             t0 * D * 2 + src_off[i], 0, 0, 0);
+  }
+}
+
+// Per-lane constants of a wavefront: its Q operands and the LDS element
+// offsets of its K and V operands within a tile.
+template <int D>
+struct Lane {
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  bf16x8 qb[KSTEPS];     // Q^T B operands: q[pos][16kk + 8j .. +7]
+  int k_rd[2][KSTEPS];   // K: key 32*kb + row, logical chunk 2kk + j
+  int v_rd[4][DB];       // V (transposed): key 16c + 4j + L/4, column 32db + dlo + 4(L%4)
+  int v_dx[4][DB];       // offset correction of the same column 8 keys later
+};
+
+// Online-softmax state of a wavefront's 32 query rows.
+template <int D>
+struct RowState {
+  float m, lsum;              // running max (log2 domain) and this lane's share of the sum
+  f32x16 acc[D / 32];         // O^T[d, rows]
+};
 
 template <int D>
-__global__ __launch_bounds__(256)
+__device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, const Lane<D>& ln,
+                                            RowState<D>& st, int t0, int pos0, int pos, int n,
+                                            int j, float scale_log2) {
+  constexpr int KSTEPS = Lane<D>::KSTEPS;
+  constexpr int DB = Lane<D>::DB;
+  // All K operands of the tile are read before the first MFMA so the LDS
+  // latency is paid once, not once per step.
+  bf16x8 ka[KSTEPS][2];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) ka[kk][kb] = load_bf16x8(ks + ln.k_rd[kb][kk]);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(ka[kk][kb], ln.qb[kk], sc[kb]);
+  // The first V operands load while the softmax runs.
+  bf16x8 va[2][DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    va[0][db] = concat(lds_read_tr16(vs + ln.v_rd[0][db]),
+                       lds_read_tr16(vs + ln.v_rd[0][db] + 8 * D + ln.v_dx[0][db]));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // sc[kb][r] = raw score of key t0 + 32*kb + 8*(r/4) + 4*j + r%4, query row
+  // `pos`.  Keys after the row (and past the end) become -inf, by a select,
+  // only in tiles that cross the diagonal.
+  if (t0 + kBN > pos0 || t0 + kBN > n) {
+    const int lim = min(pos, n - 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
+        sc[kb][r] = t <= lim ? sc[kb][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+  bf16x8 pb[4];
+  float alpha;
+  if (scale_log2 > 0.f) {
+    // max over raw scores; weights exp2(s*c - m) with one FMA each
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * scale_log2;
+    const float m_new = fmaxf(st.m, mx);   // finite: key 0 is in every row's first tile
+    alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -m_new));
+  } else {
+    // zero or negative scale: scale first, then mask-preserving max
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[kb][r] = sc[kb][r] == -INFINITY ? -INFINITY : sc[kb][r] * scale_log2;
+        mx = fmaxf(mx, sc[kb][r]);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(sc[kb][r] - m_new);
+  }
+  // the denominator sums exactly the bf16 weights PV uses (2 per dot)
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  float ps = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c][2 * e], pb[c][2 * e + 1]}, ones, ps, false);
+  st.lsum = st.lsum * alpha + ps;
+  // Rescale only when some row's running max moved.
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
+  }
+
+  // O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows], four times.  B slots
+  // of pb[c]: keys 16c + 4j + (0..3) then 16c + 8 + 4j + (0..3); the V
+  // operands of the next key chunk load during this chunk's MFMAs.
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c + 1 < 4) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        va[(c + 1) & 1][db] = concat(lds_read_tr16(vs + ln.v_rd[c + 1][db]),
+                                     lds_read_tr16(vs + ln.v_rd[c + 1][db] + 8 * D + ln.v_dx[c + 1][db]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) st.acc[db] = mfma32(va[c & 1][db], pb[c], st.acc[db]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const __bf16* __restrict__ v, float* __restrict__ out,
                          float* __restrict__ lse, int hq, int hkv, int n, int g, int gw,
                          int n_qtiles, int units, float scale_log2) {
-  constexpr int KSTEPS = D / 16;   // MFMA steps over the head dim for QK^T
-  constexpr int DB = D / 32;       // O^T row blocks
-  constexpr int PITCH = D + 8;     // bf16 elements per LDS row (16-byte pad)
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  __shared__ __align__(16) __bf16 ks[kBN * PITCH];
-  __shared__ __align__(16) __bf16 vs[kBN * PITCH];
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  constexpr int TILE = kBN * D;         // bf16 elements per K or V tile
+  constexpr int LOADS = kBN * CPR / kPrefillThreads;   // 16-byte loads per thread per tile
+  __shared__ __align__(16) __bf16 k0s[TILE];
+  __shared__ __align__(16) __bf16 v0s[TILE];
+  __shared__ __align__(16) __bf16 k1s[TILE];
+  __shared__ __align__(16) __bf16 v1s[TILE];
 
   // Workgroup -> (unit = (b, kvh, head block), q-tile), heaviest tiles first.
   int unit, qt;
@@ -67,90 +234,83 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int mq = kRows / gw;
   const int q0 = qt * mq;
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int row = lane & 31;   // query row within the wave (B/D column)
   const int j = lane >> 5;     // contraction group
   const int head = kvh * g + hb * gw + (32 * w) / mq;
   const int pos0 = q0 + (32 * w) % mq;
   const int pos = pos0 + row;
 
-  bf16x8 qb[KSTEPS];
+  Lane<D> ln;
   {
     const __bf16* qrow = q + (((size_t)b * hq + head) * n + min(pos, n - 1)) * D;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = load_bf16x8(qrow + 16 * kk + 8 * j);
-  }
-
-  float m = -INFINITY, lsum = 0.f;
-  f32x16 acc[DB];
+    for (int kk = 0; kk < KSTEPS; ++kk) ln.qb[kk] = load_bf16x8(qrow + 16 * kk + 8 * j);
 #pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-
-  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
-  const int kv_hi = min(n, q0 + mq);       // keys any row of the workgroup needs
-  const int wave_hi = min(n, pos0 + 32);   // keys this wavefront needs
-
-  for (int t0 = 0; t0 < kv_hi; t0 += kBN) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBN * CPR; i += 256) {
-      const int r = i / CPR, c = i - (i / CPR) * CPR;
-      const size_t src = kv_off + (size_t)min(t0 + r, n - 1) * D + 8 * c;
-      store_bf16x8(ks + r * PITCH + 8 * c, load_bf16x8(k + src));
-      store_bf16x8(vs + r * PITCH + 8 * c, load_bf16x8(v + src));
-    }
-    __syncthreads();
-    if (t0 >= wave_hi) continue;   // whole tile above this wave's diagonal
-
-    f32x16 sc = f32x16{};
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      sc = mfma32(load_bf16x8(ks + row * PITCH + 16 * kk + 8 * j), qb[kk], sc);
-    // sc[r] = score of key t0 + 8*(r/4) + 4*j + r%4 for query row `row`.
-    const bool diag = t0 + kBN > pos0 || t0 + kBN > n;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = sc[r] * scale_log2;
-      if (diag) {
-        const int t = t0 + 8 * (r >> 2) + 4 * j + (r & 3);
-        if (t > pos || t >= n) s = -INFINITY;
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int key = 32 * kb + row;
+        ln.k_rd[kb][kk] = key * D + swz<CPR>(key, 2 * kk + j) * 8;
       }
-      sc[r] = s;
-      mx = fmaxf(mx, s);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);   // finite: key 0 is in every row's first tile
-    const float alpha = fast_exp2(m - m_new);
-    bf16x8 pb[2];
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const __bf16 p = (__bf16)fast_exp2(sc[r] - m_new);
-      pb[r >> 3][r & 7] = p;
-      ps += (float)p;
-    }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-
-    // O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows] twice.  B slots of
-    // pb[q2]: keys 16*q2 + 4*j + (0..3) then 16*q2 + 8 + 4*j + (0..3).
     const int L = lane & 15;
     const int dlo = 16 * ((lane >> 4) & 1);   // which 16 of the 32 A rows
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const __bf16* base = vs + (16 * q2 + 4 * j + (L >> 2)) * PITCH + 32 * db + dlo + 4 * (L & 3);
-        const bf16x8 va = concat(lds_read_tr16(base), lds_read_tr16(base + 8 * PITCH));
-        acc[db] = mfma32(va, pb[q2], acc[db]);
+        const int key = 16 * c + 4 * j + (L >> 2);
+        const int col = 32 * db + dlo + 4 * (L & 3);
+        ln.v_rd[c][db] = key * D + swz<CPR>(key, col >> 3) * 8 + (col & 7);
+        ln.v_dx[c][db] = (swz<CPR>(key + 8, col >> 3) - swz<CPR>(key, col >> 3)) * 8;
       }
-    }
   }
 
-  lsum += shfl_xor(lsum, 32);
+  // K/V of this (sequence, KV head); rows >= n read as zeros.
+  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, n * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, n * D * 2);
+  // Thread tid fills physical chunks p = tid + 256*i of a tile (LDS byte
+  // 16*p); it loads the logical chunk that the swizzle places there.
+  int src_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = tid + kPrefillThreads * i;
+    const int key = p / CPR;
+    src_off[i] = key * D * 2 + swz<CPR>(key, p % CPR) * 16;
+  }
+
+  RowState<D> st;
+  st.m = -INFINITY;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < DB; ++i) st.acc[i] = f32x16{};
+
+  const int kv_hi = min(n, q0 + mq);       // keys any row of the workgroup needs
+  const int wave_hi = min(n, pos0 + 32);   // keys this wavefront needs
+  const int ntiles = (kv_hi + kBN - 1) / kBN;
+
+  issue_tile<D, LOADS>(k0s, v0s, rk, rv, src_off, w, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    // stage 0 holds tile it
+    if (it + 1 < ntiles) issue_tile<D, LOADS>(k1s, v1s, rk, rv, src_off, w, (it + 1) * kBN);
+    if (it * kBN < wave_hi) attend_tile<D>(k0s, v0s, ln, st, it * kBN, pos0, pos, n, j, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile have landed
+    __syncthreads();                 // ... everyone's, and everyone is done with stage 0
+    if (it + 1 >= ntiles) break;
+    // stage 1 holds tile it + 1
+    if (it + 2 < ntiles) issue_tile<D, LOADS>(k0s, v0s, rk, rv, src_off, w, (it + 2) * kBN);
+    if ((it + 1) * kBN < wave_hi)
+      attend_tile<D>(k1s, v1s, ln, st, (it + 1) * kBN, pos0, pos, n, j, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const float lsum = st.lsum + shfl_xor(st.lsum, 32);
   if (pos < n) {
     const float inv = 1.f / lsum;
     float* orow = out + (((size_t)b * hq + head) * n + pos) * D;
@@ -160,10 +320,10 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int r4 = 0; r4 < 4; ++r4) {
         f32x4 o4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = acc[db][4 * r4 + r] * inv;
+        for (int r = 0; r < 4; ++r) o4[r] = st.acc[db][4 * r4 + r] * inv;
         *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * j) = o4;
       }
-    if (lse != nullptr && j == 0) lse[((size_t)b * hq + head) * n + pos] = (m + __log2f(lsum)) * kLn2;
+    if (lse != nullptr && j == 0) lse[((size_t)b * hq + head) * n + pos] = (st.m + __log2f(lsum)) * kLn2;
   }
 }
 
@@ -182,11 +342,11 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, fl
   auto kp = static_cast<const __bf16*>(k);
   auto vp = static_cast<const __bf16*>(v);
   if (s.d == 128)
-    hipLaunchKernelGGL(prefill_causal_bf16<128>, grid, dim3(256), 0, stream, qp, kp, vp, out, lse,
-                       s.hq, s.hkv, s.n, g, gw, n_qtiles, units, sl2);
+    hipLaunchKernelGGL(prefill_causal_bf16<128>, grid, dim3(kPrefillThreads), 0, stream, qp, kp, vp,
+                       out, lse, s.hq, s.hkv, s.n, g, gw, n_qtiles, units, sl2);
   else
-    hipLaunchKernelGGL(prefill_causal_bf16<64>, grid, dim3(256), 0, stream, qp, kp, vp, out, lse,
-                       s.hq, s.hkv, s.n, g, gw, n_qtiles, units, sl2);
+    hipLaunchKernelGGL(prefill_causal_bf16<64>, grid, dim3(kPrefillThreads), 0, stream, qp, kp, vp,
+                       out, lse, s.hq, s.hkv, s.n, g, gw, n_qtiles, units, sl2);
   return hipGetLastError();
 }
 
