@@ -14,7 +14,7 @@ timed region and rotated over several copies so the 256 MB MALL cannot serve
 repeated steps.  Kernel durations come from HIP events on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
-  python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,14 +36,19 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "GQA decode KV-read GB/s (% of HBM peak) + causal prefill TFLOP/s (% MFMA)"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", f)
-                  for f in ("decode.hip", "prefill.hip", "gqa_device.hpp", "gqa_launch.hpp")]
+CSRC = os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc")
+# the sources each measured kernel is built from (a counter entry is used only
+# while their digest is unchanged)
+KERNEL_SOURCES = {
+    "decode_split": ("decode.hip", "api.hip", "gqa_device.hpp", "gqa_launch.hpp"),
+    "prefill_causal": ("prefill.hip", "gqa_device.hpp", "gqa_launch.hpp"),
+}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -92,48 +97,93 @@ def event_time_ms(fn, iters, torch):
 
 
 def load_counters(kernel: str, workload: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, only if
-    the kernel sources are unchanged since they were taken."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
+    committed rocprofv3 counter runs, or None when there is no entry or the
+    kernel's sources changed since the counters were taken."""
     try:
         with open(COUNTERS) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(f"{kernel}|{workload}")
-    if not entry or entry.get("source_digest") != kernel_source_digest():
+    entry = data.get("kernels", {}).get(f"{kernel}|{workload}")
+    if not entry or entry.get("source_digest") != kernel_source_digest(kernel):
         return None
     return entry.get("traffic_bytes")
 
 
-def cpu_baseline_decode(inp, budget_s: float):
-    """Time the float64 oracle on the host over as many whole sequences of
-    the workload as fit in about `budget_s` seconds."""
+CALIBRATION_BYTES = 256 * 2 ** 20   # read and written by the --calibration-copy kernel
+COUNTED_KERNELS = {   # kernel-name substring -> (entry kernel, sources key)
+    "decode_split_bf16": "decode_split",
+    "prefill_causal_bf16": "prefill_causal",
+}
+
+
+def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
+    """Build profiles/counters.json from two rocprofv3 --pmc runs of
+    ``bench.py --calibration-copy`` (one with FETCH_SIZE, one with WRITE_SIZE).
+
+    Each counter (KiB per dispatch) is scaled by the factor that maps its
+    reading for the calibration copy kernel (the last elementwise dispatch:
+    256 MiB read, 256 MiB written) onto the bytes that kernel moves."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        calib = [float(r["Counter_Value"]) for r in rows if "elementwise" in r["Kernel_Name"]]
+        if not calib:
+            raise SystemExit(f"{path}: no calibration copy dispatch (run bench.py --calibration-copy)")
+        factor = CALIBRATION_BYTES / (calib[-1] * 1024)
+        vals = {}
+        for r in rows:
+            for sub, name in COUNTED_KERNELS.items():
+                if sub in r["Kernel_Name"]:
+                    vals.setdefault(name, []).append(float(r["Counter_Value"]))
+        return factor, {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+    ff, fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    wf, write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    out = {"calibration": {"kernel": "torch.neg over 64 Mi float32 (256 MiB read + 256 MiB written)",
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": {}}
+    for name in fetch:
+        wl = "prefill-4k" if name == "prefill_causal" else workload
+        fb, wb = fetch[name] * 1024 * ff, write.get(name, 0.0) * 1024 * wf
+        out["kernels"][f"{name}|{wl}"] = {
+            "source_digest": kernel_source_digest(name),
+            "fetch_kib_raw": round(fetch[name], 1), "write_kib_raw": round(write.get(name, 0.0), 1),
+            "dispatches": [nf[name], nw.get(name, 0)],
+            "fetch_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb)}
+    return out
+
+
+def cpu_baseline_decode(inp, budget_s: float, max_passes: int = 50):
+    """Time the float64 oracle on the host, one whole sequence of the workload
+    per call, cycling over the batch until about `budget_s` seconds of oracle
+    time have been spent (input conversion to float64 is not timed)."""
     from threadpoolctl import threadpool_info, threadpool_limits
     import gqa_inputs as gi
     import oracle
     cores = min(16, len(os.sched_getaffinity(0)))
     cfg = inp.cfg
-    done, t_used, bytes_done = 0, 0.0, 0
+    elem = 2 if cfg.dtype == "bf16" else 4
+    calls, t_used, bytes_done = 0, 0.0, 0
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        for b in range(cfg.batch):
+        while t_used < budget_s and calls < max_passes * cfg.batch:
+            b = calls % cfg.batch
             q = gi.to_f64(inp.q[b:b + 1], cfg.dtype)
-            k = inp.k_cache[b:b + 1]
-            v = inp.v_cache[b:b + 1]
+            kf = gi.to_f64(inp.k_cache[b:b + 1], cfg.dtype)
+            vf = gi.to_f64(inp.v_cache[b:b + 1], cfg.dtype)
             t0 = time.perf_counter()
-            kf = gi.to_f64(k, cfg.dtype)
-            vf = gi.to_f64(v, cfg.dtype)
             oracle.decode(q, kf, vf, inp.seq_lens[b:b + 1], cfg.scale)
             t_used += time.perf_counter() - t0
-            done += 1
-            bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim,
-                                          2 if cfg.dtype == "bf16" else 4)
-            if t_used >= budget_s:
-                break
+            calls += 1
+            bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim, elem)
     return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} sequences of the same workload (float64 numpy oracle, "
-                      f"explicit K/V repeat), {t_used:.1f} s wall"}
+            "sample": f"{calls} single-sequence oracle calls cycling over the {cfg.batch} sequences of the "
+                      f"same workload ({calls / cfg.batch:.2f} passes; float64 numpy, explicit K/V repeat), "
+                      f"{t_used:.1f} s of oracle time; value = K/V bytes of the bf16 cache / oracle time"}
 
 
 def main():
@@ -141,14 +191,28 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4"])
+    ap.add_argument("--workload", default="llama3-8b", choices=["llama3-8b", "wide-group", "mqa-128k"])
+    ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters.json from two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--print-digests", action="store_true",
+                    help="print the source digest of each measured kernel and exit")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run one plain device copy of 256 MiB (counter calibration)")
+                    help="also run one plain 256 MiB device copy kernel (counter calibration)")
     args = ap.parse_args()
+    if args.record_counters:
+        data = record_counters(*args.record_counters, args.workload)
+        with open(COUNTERS, "w") as f:
+            json.dump(data, f, indent=1)
+            f.write("\n")
+        print(json.dumps(data))
+        return
+    if args.print_digests:
+        print(json.dumps({k: kernel_source_digest(k) for k in KERNEL_SOURCES}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GQA kernels here run on a single device "
               "and no multi-GPU path is built; run with --gpus 1.", file=sys.stderr)
@@ -237,7 +301,7 @@ def main():
     }
 
     if not args.no_prefill:
-        pc = gi.CONFIGS["c5"]
+        pc = gi.CONFIGS["prefill-4k"]
         p = gi.make_prefill(pc)
         pq, pk, pv = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (p.q, p.k, p.v))
         pout = torch.empty(pc.batch, pc.num_q_heads, pc.seq_len, pc.head_dim, dtype=torch.float32,
@@ -258,16 +322,18 @@ def main():
             "roofline": {"kernel": "prefill_causal_bf16", "bound": "mfma", "achieved": round(tf, 2),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "traffic": load_counters("prefill_causal", "c5"),
+                         "traffic": load_counters("prefill_causal", "prefill-4k"),
                          "algorithmic_flops": fl,
                          "algorithmic_bytes": prefill_bytes(pc.batch, pc.num_q_heads, pc.num_kv_heads,
                                                             pc.seq_len, pc.head_dim)},
         }
 
     if args.calibration_copy:
-        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
+        # one elementwise kernel that reads 256 MiB and writes 256 MiB, the
+        # known-size launch the FETCH_SIZE / WRITE_SIZE counters are scaled by
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:

@@ -7,14 +7,14 @@ oracle and the GPU path can consume its arrays without sharing method code.
 
 Workloads (the five shapes the library is measured and checked on):
 
-  c1  tiny decode, fp32: B=1, Hq=8, Hkv=2, d=64, 256 cached tokens
-  c2  Llama-3-8B-shaped decode, bf16: B=32, Hq=32, Hkv=8, d=128, 8192 tokens
-  c3  wide-group decode, bf16: B=64, Hq=32, Hkv=2, d=128, ragged lengths
+  tiny-f32    tiny decode, fp32: B=1, Hq=8, Hkv=2, d=64, 256 cached tokens
+  llama3-8b   Llama-3-8B-shaped decode, bf16: B=32, Hq=32, Hkv=8, d=128, 8192 tokens
+  wide-group  wide-group decode, bf16: B=64, Hq=32, Hkv=2, d=128, ragged lengths
       drawn uniformly from [1024, 32768] (inclusive), cache capacity 32768
-  c4  MQA long-context decode, bf16: B=4, Hq=16, Hkv=1, d=128, 131072 tokens
-  c5  causal prefill, bf16: B=2, Hq=32, Hkv=8, d=128, N=4096
+  mqa-128k    MQA long-context decode, bf16: B=4, Hq=16, Hkv=1, d=128, 131072 tokens
+  prefill-4k  causal prefill, bf16: B=2, Hq=32, Hkv=8, d=128, N=4096
 
-Recipe: seed = 1000 + workload index; ``SeedSequence(seed).spawn(4)`` gives
+Recipe: seeds 1001..1005 in the order listed above; ``SeedSequence(seed).spawn(4)`` gives
 independent PCG64 streams for (lengths, Q, K, V) in that order; values are
 i.i.d. standard normal drawn as float32 and, for bf16 workloads, rounded to
 bfloat16 with round-to-nearest-even.  Cache slots past a sequence's length
@@ -75,11 +75,11 @@ class PrefillConfig:
 
 
 CONFIGS = {
-    "c1": DecodeConfig("tiny-decode-fp32", "f32", 1, 8, 2, 64, 256, 256, 256, 1001),
-    "c2": DecodeConfig("llama3-8b-decode-bf16", "bf16", 32, 32, 8, 128, 8192, 8192, 8192, 1002),
-    "c3": DecodeConfig("wide-group-ragged-decode-bf16", "bf16", 64, 32, 2, 128, 32768, 1024, 32768, 1003),
-    "c4": DecodeConfig("mqa-long-decode-bf16", "bf16", 4, 16, 1, 128, 131072, 131072, 131072, 1004),
-    "c5": PrefillConfig("causal-prefill-bf16", "bf16", 2, 32, 8, 128, 4096, 1005),
+    "tiny-f32": DecodeConfig("tiny-decode-fp32", "f32", 1, 8, 2, 64, 256, 256, 256, 1001),
+    "llama3-8b": DecodeConfig("llama3-8b-decode-bf16", "bf16", 32, 32, 8, 128, 8192, 8192, 8192, 1002),
+    "wide-group": DecodeConfig("wide-group-ragged-decode-bf16", "bf16", 64, 32, 2, 128, 32768, 1024, 32768, 1003),
+    "mqa-128k": DecodeConfig("mqa-long-decode-bf16", "bf16", 4, 16, 1, 128, 131072, 131072, 131072, 1004),
+    "prefill-4k": PrefillConfig("causal-prefill-bf16", "bf16", 2, 32, 8, 128, 4096, 1005),
 }
 
 

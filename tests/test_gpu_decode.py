@@ -46,12 +46,12 @@ def check_rows(inp, got, pairs):
     return worst
 
 
-def test_c1_tiny_fp32_full_parity():
+def test_tiny_fp32_decode_full_parity():
     need_gpu()
-    inp = gi.make_decode(gi.CONFIGS["c1"])
-    say("c1", gi.describe(inp.cfg))
+    inp = gi.make_decode(gi.CONFIGS["tiny-f32"])
+    say("tiny-f32", gi.describe(inp.cfg))
     err = max_err(run_decode(inp), oracle_full(inp))
-    say("c1 max err", err)
+    say("tiny-f32 max err", err)
     assert err <= TOL["f32"]
 
 
@@ -88,39 +88,39 @@ def test_small_shapes_full_parity(case):
             assert np.all(got[b] == 0.0)
 
 
-def test_c2_llama3_full_parity():
+def test_llama3_8b_decode_full_parity():
     need_gpu()
-    inp = gi.make_decode(gi.CONFIGS["c2"])
-    say("c2", gi.describe(inp.cfg))
+    inp = gi.make_decode(gi.CONFIGS["llama3-8b"])
+    say("llama3-8b", gi.describe(inp.cfg))
     got = run_decode(inp)
     err = max_err(got, oracle_full(inp))
-    say("c2 max err", err)
+    say("llama3-8b max err", err)
     assert err <= TOL["bf16"]
 
 
-def test_c3_ragged_wide_group_sampled():
+def test_wide_group_ragged_decode_sampled():
     need_gpu()
-    inp = gi.make_decode(gi.CONFIGS["c3"])
-    say("c3", gi.describe(inp.cfg), "sum T", int(inp.seq_lens.sum()))
+    inp = gi.make_decode(gi.CONFIGS["wide-group"])
+    say("wide-group", gi.describe(inp.cfg), "sum T", int(inp.seq_lens.sum()))
     got = run_decode(inp)
     lens = inp.seq_lens
     bs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
     pairs = [(b, h) for b in bs for h in (0, 1, 15, 16, 17, 31)]
     err = check_rows(inp, got, pairs)
-    say("c3 sampled max err", err)
+    say("wide-group sampled max err", err)
     assert err <= TOL["bf16"]
     # all rows: finite and inside the hull of the attended values (per coordinate)
     assert np.all(np.isfinite(got))
 
 
-def test_c4_mqa_long_context_sampled():
+def test_mqa_128k_decode_sampled():
     need_gpu()
-    inp = gi.make_decode(gi.CONFIGS["c4"])
-    say("c4", gi.describe(inp.cfg))
+    inp = gi.make_decode(gi.CONFIGS["mqa-128k"])
+    say("mqa-128k", gi.describe(inp.cfg))
     got = run_decode(inp)
     pairs = [(b, h) for b in range(4) for h in (0, 5, 15)] + [(0, h) for h in range(16)]
     err = check_rows(inp, got, sorted(set(pairs)))
-    say("c4 sampled max err", err)
+    say("mqa-128k sampled max err", err)
     assert err <= TOL["bf16"]
 
 

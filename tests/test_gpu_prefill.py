@@ -51,11 +51,11 @@ def test_small_full_parity(case):
             assert np.array_equal(out[b, h, 0], gi.bf16_bits_to_f32(p.v[b, h // g, 0]))
 
 
-def test_c5_full_size_sampled_rows():
+def test_prefill_4k_full_size_sampled_rows():
     need_gpu()
-    cfg = gi.CONFIGS["c5"]
+    cfg = gi.CONFIGS["prefill-4k"]
     p = gi.make_prefill(cfg)
-    say("c5", gi.describe(cfg))
+    say("prefill-4k", gi.describe(cfg))
     out, lse = run_prefill(p)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     rng = np.random.default_rng(0)
@@ -68,7 +68,7 @@ def test_c5_full_size_sampled_rows():
             ref, ref_lse = oracle.prefill_causal_rows(gi.to_f64(p.q[b, h, rows], "bf16"), kb, vb, rows,
                                                       h, cfg.num_q_heads, cfg.scale)
             worst = max(worst, max_err(out[b, h, rows], ref), max_err(lse[b, h, rows], ref_lse))
-    say("c5 sampled max err", worst)
+    say("prefill-4k sampled max err", worst)
     assert worst <= TOL["bf16"]
 
 

@@ -17,7 +17,7 @@ def test_bf16_rounding_matches_torch_rne():
 
 
 def test_decode_inputs_deterministic_and_shaped():
-    cfg = gi.CONFIGS["c1"]
+    cfg = gi.CONFIGS["tiny-f32"]
     a = gi.make_decode(cfg)
     b = gi.make_decode(cfg)
     assert a.q.shape == (1, 8, 64) and a.k_cache.shape == (1, 2, 256, 64)
@@ -31,7 +31,7 @@ def test_decode_inputs_deterministic_and_shaped():
 
 
 def test_ragged_lengths_and_padding():
-    cfg = gi.CONFIGS["c3"]
+    cfg = gi.CONFIGS["wide-group"]
     lens = gi.make_seq_lens(cfg)
     assert lens.dtype == np.int32 and lens.shape == (64,)
     assert lens.min() >= 1024 and lens.max() <= 32768
@@ -52,7 +52,7 @@ def test_prefill_inputs():
 
 def test_workload_table():
     c = gi.CONFIGS
-    assert (c["c2"].batch, c["c2"].num_q_heads, c["c2"].num_kv_heads, c["c2"].head_dim, c["c2"].max_seq_len) == (32, 32, 8, 128, 8192)
-    assert (c["c4"].batch, c["c4"].num_q_heads, c["c4"].num_kv_heads, c["c4"].max_seq_len) == (4, 16, 1, 131072)
-    assert (c["c5"].batch, c["c5"].num_q_heads, c["c5"].num_kv_heads, c["c5"].seq_len) == (2, 32, 8, 4096)
-    assert [c[k].seed for k in ("c1", "c2", "c3", "c4", "c5")] == [1001, 1002, 1003, 1004, 1005]
+    assert (c["llama3-8b"].batch, c["llama3-8b"].num_q_heads, c["llama3-8b"].num_kv_heads, c["llama3-8b"].head_dim, c["llama3-8b"].max_seq_len) == (32, 32, 8, 128, 8192)
+    assert (c["mqa-128k"].batch, c["mqa-128k"].num_q_heads, c["mqa-128k"].num_kv_heads, c["mqa-128k"].max_seq_len) == (4, 16, 1, 131072)
+    assert (c["prefill-4k"].batch, c["prefill-4k"].num_q_heads, c["prefill-4k"].num_kv_heads, c["prefill-4k"].seq_len) == (2, 32, 8, 4096)
+    assert [c[k].seed for k in ("tiny-f32", "llama3-8b", "wide-group", "mqa-128k", "prefill-4k")] == [1001, 1002, 1003, 1004, 1005]
