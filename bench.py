@@ -83,17 +83,25 @@ def prefill_bytes(b, hq, hkv, n, d):
 
 # ---------------------------------------------------------------------------
 
-def event_time_ms(fn, iters, torch):
-    """Average duration of fn() over `iters` back-to-back calls, by HIP events
-    on the current stream."""
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(iters):
-        fn(i)
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / iters
+def event_time_ms(fn, iters, torch, batches: int = 5):
+    """Duration of fn() per call: `batches` runs of `iters` back-to-back calls,
+    each bracketed by HIP events on the current stream; the median batch
+    average is returned (GPU clocks move under sustained load)."""
+    per = max(1, iters // batches)
+    times = []
+    done = 0
+    for _ in range(batches):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(per):
+            fn(done)
+            done += 1
+        stop.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(stop) / per)
+    times.sort()
+    return times[len(times) // 2]
 
 
 def load_counters(kernel: str, workload: str):

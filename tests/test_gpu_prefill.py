@@ -29,6 +29,10 @@ SMALL = [
     (1, 16, 1, 200, 128),    # MQA, group 16
     (1, 4, 2, 1, 128),       # a single token
     (1, 8, 4, 33, 64),       # group 2
+    (1, 8, 4, 1000, 128),    # group 2, 64 positions per q-tile, even q-tile count
+    (1, 16, 2, 515, 128),    # group 8 (two head blocks), odd q-tile count
+    (2, 4, 1, 640, 64),      # MQA-style group 4, d = 64
+    (1, 3, 3, 389, 128),     # MHA, 128 positions per q-tile, split pairs
 ]
 
 
@@ -91,3 +95,17 @@ def test_identical_queries_in_group_identical_rows():
     out, _ = run_prefill(p)
     assert np.array_equal(out[0, 0], out[0, 1])
     assert not np.allclose(out[0, 0], out[0, 2])
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.07], ids=["zero", "negative"])
+def test_nonpositive_scale(scale):
+    need_gpu()
+    p = gi.small_prefill(1, 8, 2, 200, 128, seed=53)
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    out, lse = gqa.gqa_prefill_causal(q, k, v, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.prefill_causal(gi.to_f64(p.q, "bf16"), gi.to_f64(p.k, "bf16"),
+                                         gi.to_f64(p.v, "bf16"), scale, return_lse=True)
+    err, lerr = max_err(out.cpu().numpy(), ref), max_err(lse.cpu().numpy(), ref_lse)
+    say("scale", scale, "max err", err, "lse err", lerr)
+    assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
