@@ -215,3 +215,49 @@ def small_prefill(batch: int, num_q_heads: int, num_kv_heads: int, seq_len: int,
     cfg = PrefillConfig(f"small-{seed}", "bf16", batch, num_q_heads, num_kv_heads,
                         head_dim, seq_len, seed)
     return make_prefill(cfg)
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache (storage layout only; no attention arithmetic)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PagedInputs:
+    """Decode inputs whose K/V live in a shared pool of fixed-size pages.
+
+    k_pages, v_pages: [num_pages, Hkv, page_size, d]; block_table[b, i] is the
+    pool index of the page holding tokens i*page_size .. (i+1)*page_size - 1 of
+    sequence b, or -1 where the sequence has no such page.  Pool order is a
+    seeded random permutation; pages no sequence uses are filled with NaN."""
+    cfg: DecodeConfig
+    q: np.ndarray
+    k_pages: np.ndarray
+    v_pages: np.ndarray
+    block_table: np.ndarray   # [B, max_pages] int32
+    seq_lens: np.ndarray      # [B] int32
+    page_size: int
+
+
+def make_paged(inp: DecodeInputs, page_size: int, spare_pages: int = 7, seed: int = 7) -> PagedInputs:
+    """Scatter a contiguous decode cache into a permuted page pool."""
+    cfg = inp.cfg
+    B, Hkv, T, d = inp.k_cache.shape
+    max_pages = -(-T // page_size)
+    used = [-(-int(t) // page_size) for t in inp.seq_lens]
+    n_pool = sum(used) + spare_pages
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    perm = rng.permutation(n_pool).astype(np.int32)
+    fill = BF16_NAN_BITS if cfg.dtype == "bf16" else np.float32(np.nan)
+    k_pages = np.full((n_pool, Hkv, page_size, d), fill, dtype=inp.k_cache.dtype)
+    v_pages = np.full((n_pool, Hkv, page_size, d), fill, dtype=inp.v_cache.dtype)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        for i in range(used[b]):
+            pid = int(perm[nxt])
+            nxt += 1
+            table[b, i] = pid
+            lo, hi = i * page_size, min((i + 1) * page_size, T)
+            k_pages[pid, :, :hi - lo] = inp.k_cache[b, :, lo:hi]
+            v_pages[pid, :, :hi - lo] = inp.v_cache[b, :, lo:hi]
+    return PagedInputs(cfg, inp.q, k_pages, v_pages, table, inp.seq_lens, page_size)

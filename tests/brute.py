@@ -56,3 +56,25 @@ def brute_prefill(q, k, v, scale):
             heads.append(rows)
         out.append(heads)
     return out
+
+
+def brute_decode_paged(q, k_pages, v_pages, block_table, seq_lens, page_size, scale):
+    """Decode through a block table: token t of sequence b is row t % page_size
+    of page block_table[b][t // page_size]; pools are [page][kv][row][i]."""
+    B, Hq = len(q), len(q[0])
+    Hkv = len(k_pages[0])
+    g = Hq // Hkv
+    out = []
+    for b in range(B):
+        T = int(seq_lens[b])
+        rows = []
+        for h in range(Hq):
+            kv = h // g
+            keys, vals = [], []
+            for t in range(T):
+                page = int(block_table[b][t // page_size])
+                keys.append(list(k_pages[page][kv][t % page_size]))
+                vals.append(list(v_pages[page][kv][t % page_size]))
+            rows.append(_attend(list(q[b][h]), keys, vals, scale) if T else [0.0] * len(q[b][h]))
+        out.append(rows)
+    return out
