@@ -14,7 +14,8 @@ timed region and rotated over several copies so the 256 MB MALL cannot serve
 repeated steps.  Kernel durations come from HIP events on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
-  python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|
+                  paged-llama3-8b|paged-wide-group] [--page-size P] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -164,10 +165,11 @@ def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
     return out
 
 
-def cpu_baseline_decode(inp, budget_s: float, max_passes: int = 50):
+def cpu_baseline_decode(inp, budget_s: float, pg=None, max_passes: int = 50):
     """Time the float64 oracle on the host, one whole sequence of the workload
     per call, cycling over the batch until about `budget_s` seconds of oracle
-    time have been spent (input conversion to float64 is not timed)."""
+    time have been spent (input conversion to float64 is not timed).  For a
+    paged workload the oracle is decode_paged over that sequence's pages."""
     from threadpoolctl import threadpool_info, threadpool_limits
     import gqa_inputs as gi
     import oracle
@@ -180,17 +182,27 @@ def cpu_baseline_decode(inp, budget_s: float, max_passes: int = 50):
         while t_used < budget_s and calls < max_passes * cfg.batch:
             b = calls % cfg.batch
             q = gi.to_f64(inp.q[b:b + 1], cfg.dtype)
-            kf = gi.to_f64(inp.k_cache[b:b + 1], cfg.dtype)
-            vf = gi.to_f64(inp.v_cache[b:b + 1], cfg.dtype)
-            t0 = time.perf_counter()
-            oracle.decode(q, kf, vf, inp.seq_lens[b:b + 1], cfg.scale)
+            if pg is None:
+                kf = gi.to_f64(inp.k_cache[b:b + 1], cfg.dtype)
+                vf = gi.to_f64(inp.v_cache[b:b + 1], cfg.dtype)
+                t0 = time.perf_counter()
+                oracle.decode(q, kf, vf, inp.seq_lens[b:b + 1], cfg.scale)
+            else:
+                n = -(-int(inp.seq_lens[b]) // pg.page_size)
+                ids = pg.block_table[b, :n]
+                kf = gi.to_f64(pg.k_pages[ids], cfg.dtype)
+                vf = gi.to_f64(pg.v_pages[ids], cfg.dtype)
+                table = np.arange(n, dtype=np.int32)[None, :]
+                t0 = time.perf_counter()
+                oracle.decode_paged(q, kf, vf, table, inp.seq_lens[b:b + 1], pg.page_size, cfg.scale)
             t_used += time.perf_counter() - t0
             calls += 1
             bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim, elem)
+    what = "decode_paged" if pg is not None else "decode"
     return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle",
-            "sample": f"{calls} single-sequence oracle calls cycling over the {cfg.batch} sequences of the "
-                      f"same workload ({calls / cfg.batch:.2f} passes; float64 numpy, explicit K/V repeat), "
+            "sample": f"{calls} single-sequence oracle.{what} calls cycling over the {cfg.batch} sequences of "
+                      f"the same workload ({calls / cfg.batch:.2f} passes; float64 numpy, explicit K/V repeat), "
                       f"{t_used:.1f} s of oracle time; value = K/V bytes of the bf16 cache / oracle time"}
 
 
@@ -199,7 +211,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama3-8b", choices=["llama3-8b", "wide-group", "mqa-128k"])
+    ap.add_argument("--workload", default="llama3-8b",
+                    choices=["llama3-8b", "wide-group", "mqa-128k", "paged-llama3-8b", "paged-wide-group"])
+    ap.add_argument("--page-size", type=int, default=16, help="tokens per page for the paged-* workloads")
     ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/counters.json from two rocprofv3 --pmc counter CSVs and exit")
     ap.add_argument("--print-digests", action="store_true",
@@ -236,7 +250,8 @@ def main():
     gqa.load_library()   # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
 
-    cfg = gi.CONFIGS[args.workload]
+    paged = args.workload.startswith("paged-")
+    cfg = gi.CONFIGS[args.workload[len("paged-"):] if paged else args.workload]
     inp = gi.make_decode(cfg)
     elem = 2 if cfg.dtype == "bf16" else 4
     dt = gqa.GQA_BF16 if cfg.dtype == "bf16" else gqa.GQA_F32
@@ -251,21 +266,38 @@ def main():
         return torch.from_numpy(a).cuda()
 
     q = to_dev(inp.q)
-    k0, v0 = to_dev(inp.k_cache), to_dev(inp.v_cache)
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    pg = None
+    if paged:
+        # the same cache scattered into a permuted pool of pages
+        pg = gi.make_paged(inp, page_size=args.page_size)
+        inp.k_cache = inp.v_cache = None
+        k0, v0 = to_dev(pg.k_pages), to_dev(pg.v_pages)
+        table = torch.from_numpy(pg.block_table).cuda()
+        T = pg.block_table.shape[1] * args.page_size
+    else:
+        k0, v0 = to_dev(inp.k_cache), to_dev(inp.v_cache)
     ks = [k0] + [k0.clone() for _ in range(rot - 1)]
     vs = [v0] + [v0.clone() for _ in range(rot - 1)]
-    lens = torch.from_numpy(inp.seq_lens).cuda()
     plan = gqa.gqa_decode_plan(B, Hq, Hkv, d, T, dt, args.split_tokens)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
 
     def step(i):
-        gqa.gqa_decode(q, ks[i % rot], vs[i % rot], lens, scale=cfg.scale, out=out, workspace=ws,
-                       split_tokens=args.split_tokens)
+        if paged:
+            gqa.gqa_decode_paged(q, ks[i % rot], vs[i % rot], table, lens, scale=cfg.scale, out=out,
+                                 workspace=ws, split_tokens=args.split_tokens)
+        else:
+            gqa.gqa_decode(q, ks[i % rot], vs[i % rot], lens, scale=cfg.scale, out=out, workspace=ws,
+                           split_tokens=args.split_tokens)
 
     def split_only(i):
-        gqa.gqa_decode_split(q, ks[i % rot], vs[i % rot], lens, out, ws, scale=cfg.scale,
-                             split_tokens=args.split_tokens)
+        if paged:
+            gqa.gqa_decode_paged(q, ks[i % rot], vs[i % rot], table, lens, scale=cfg.scale, out=out,
+                                 workspace=ws, split_tokens=args.split_tokens, stage="split")
+        else:
+            gqa.gqa_decode_split(q, ks[i % rot], vs[i % rot], lens, out, ws, scale=cfg.scale,
+                                 split_tokens=args.split_tokens)
 
     for i in range(args.warmup):
         step(i)
@@ -277,6 +309,8 @@ def main():
     ms_split = event_time_ms(split_only, args.steps, torch)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     split_bytes = decode_split_bytes(inp.seq_lens, Hq, Hkv, d, elem)
+    if paged:   # plus one read of each block-table entry in use
+        split_bytes += 4 * int(np.sum(-(-inp.seq_lens.astype(np.int64) // args.page_size)))
     achieved = split_bytes / (ms_split * 1e-3) / 1e9
     traffic = load_counters("decode_split", args.workload)
 
@@ -293,14 +327,16 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": gi.describe(cfg), "global_batch": B, "seq_len": T,
+        "config": {"workload": (f"paged (page {args.page_size}) " if paged else "") + gi.describe(cfg),
+                   "global_batch": B, "seq_len": cfg.max_seq_len,
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
                    "range_tokens": plan.range_tokens or "auto", "workgroups": plan.workgroups,
                    "kv_rotation_copies": rot, "parallelism": "single-gpu"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "decode_tflops": round(decode_flops(inp.seq_lens, Hq, d) / (ms_step * 1e-3) / 1e12, 3),
-        "roofline": {"kernel": "decode_split_bf16" if cfg.dtype == "bf16" else "decode_split_f32",
+        "roofline": {"kernel": ("decode_split_bf16 (paged)" if paged else "decode_split_bf16")
+                     if cfg.dtype == "bf16" else "decode_split_f32",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": split_bytes,
@@ -345,7 +381,7 @@ def main():
         torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget, pg)
 
     print(json.dumps(result), flush=True)
 

@@ -77,6 +77,11 @@ def load_library():
     lib.gqa_decode_split.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
     lib.gqa_decode_merge.restype = I32
     lib.gqa_decode_merge.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
+    lib.gqa_decode_paged.restype = I32
+    lib.gqa_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32,
+                                     P, I64, P]
+    lib.gqa_decode_paged_split.restype = I32
+    lib.gqa_decode_paged_split.argtypes = lib.gqa_decode_paged.argtypes
     lib.gqa_prefill_causal.restype = I32
     lib.gqa_prefill_causal.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P]
     _lib = lib
@@ -173,6 +178,48 @@ def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check("gqa_decode", lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                         _ptr(out), B, Hq, Hkv, d, tcap, scale, dt, split_tokens,
                                         _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def _paged_args(q, k_pages, v_pages, block_table, seq_lens):
+    _require(q.dim() == 3 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape,
+             "expected q [B,Hq,d] and k/v pages [num_pages,Hkv,page_size,d]")
+    _require(block_table.dim() == 2 and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, max_pages]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens must be int32 [B]")
+    B, Hq, d = q.shape
+    num_pages, Hkv, page_size, d2 = k_pages.shape
+    _require(d == d2 and block_table.shape[0] == B and seq_lens.shape[0] == B, "shape mismatch")
+    _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the pages must share a dtype")
+    dev = _on_gpu(q, k_pages, v_pages, block_table, seq_lens)
+    return dev, B, Hq, Hkv, d, num_pages, page_size, block_table.shape[1], _dtype_code(q)
+
+
+def gqa_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                     block_table: torch.Tensor, seq_lens: torch.Tensor, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     split_tokens: int = 0, stage: str = "both") -> torch.Tensor:
+    """One GQA decode step over a paged cache; returns out [B, Hq, d] float32.
+
+    k_pages, v_pages: [num_pages, Hkv, page_size, d] bf16; block_table:
+    [B, max_pages] int32 (see gqa.h).  stage="split" runs only the first
+    stage (gqa_decode_paged_split); gqa_decode_merge with max_seq_len =
+    max_pages * page_size completes it."""
+    dev, B, Hq, Hkv, d, num_pages, page_size, max_pages, dt = _paged_args(q, k_pages, v_pages, block_table,
+                                                                         seq_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    plan = gqa_decode_plan(B, Hq, Hkv, d, max_pages * page_size, dt, split_tokens)
+    ws = _workspace(workspace, plan, dev)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, d), "out must be float32 [B,Hq,d]")
+    _on_gpu(q, out)
+    _require(stage in ("both", "split"), "stage must be 'both' or 'split'")
+    lib = load_library()
+    fn = lib.gqa_decode_paged if stage == "both" else lib.gqa_decode_paged_split
+    _check("gqa_decode_paged" if stage == "both" else "gqa_decode_paged_split", fn(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d,
+        page_size, num_pages, max_pages, scale, dt, split_tokens, _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
 

@@ -181,6 +181,69 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
 }
 
+static int32_t paged_prepare(const void* q, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens, float* out,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t num_pages,
+                             int32_t max_pages_per_seq, float scale, int32_t dtype,
+                             int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                             gqa::DecodeShape* s, gqa::PagedKV* pk) {
+  if (!out || !block_table) return GQA_ERR_NULL;
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 || num_pages < 1 ||
+      max_pages_per_seq < 1)
+    return GQA_ERR_SHAPE;
+  const int64_t tcap = (int64_t)max_pages_per_seq * page_size;
+  if (tcap > INT32_MAX) return GQA_ERR_SHAPE;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  gqa::DecodeWorkspace ws;
+  const int32_t st = decode_prepare(q, k_pages, v_pages, seq_lens, workspace, workspace_bytes, batch,
+                                    num_q_heads, num_kv_heads, head_dim, (int32_t)tcap, scale, dtype,
+                                    split_tokens, s, &ws);
+  if (st != GQA_OK) return st;
+  if (!aligned(out, 16) || !aligned(block_table, 4)) return GQA_ERR_ALIGN;
+  int log2 = 0;
+  while ((1 << log2) < page_size) ++log2;
+  *pk = gqa::PagedKV{block_table, max_pages_per_seq, num_pages, log2};
+  return GQA_OK;
+}
+
+int32_t gqa_decode_paged_split(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, float* out,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t page_size, int32_t num_pages,
+                               int32_t max_pages_per_seq, float scale, int32_t dtype,
+                               int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  gqa::DecodeShape s;
+  gqa::PagedKV pk;
+  const int32_t st = paged_prepare(q, k_pages, v_pages, block_table, seq_lens, out, batch, num_q_heads,
+                                   num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq, scale,
+                                   dtype, split_tokens, workspace, workspace_bytes, &s, &pk);
+  if (st != GQA_OK) return st;
+  return hip_status(gqa::launch_decode_split(q, k_pages, v_pages, seq_lens, out, static_cast<char*>(workspace),
+                                             s, static_cast<hipStream_t>(stream), pk));
+}
+
+int32_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens, float* out,
+                         int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t page_size, int32_t num_pages,
+                         int32_t max_pages_per_seq, float scale, int32_t dtype,
+                         int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+  gqa::DecodeShape s;
+  gqa::PagedKV pk;
+  int32_t st = paged_prepare(q, k_pages, v_pages, block_table, seq_lens, out, batch, num_q_heads,
+                             num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq, scale, dtype,
+                             split_tokens, workspace, workspace_bytes, &s, &pk);
+  if (st != GQA_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = hip_status(gqa::launch_decode_split(q, k_pages, v_pages, seq_lens, out, base, s, hs, pk));
+  if (st != GQA_OK) return st;
+  return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
+}
+
 int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out, float* lse,
                            int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t seq_len, int32_t head_dim, float scale, int32_t dtype,

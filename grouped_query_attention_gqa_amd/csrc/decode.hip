@@ -223,17 +223,53 @@ __device__ __forceinline__ void load_tile(DecodeTile<D>& t, __amdgpu_buffer_rsrc
     t.v[i] = buffer_load_bf16x8<kCacheStream>(rv, tile_bytes + v_off + i * RPI * ROW, 0);
 }
 
+// The same tile from a paged cache: every row the lane loads is looked up in
+// the block table.  Rows past the segment end are clamped to its last token
+// (their scores are masked, and their values are finite cache contents), and
+// page indices are clamped into the pool, so no access leaves the K/V pools
+// whatever the table holds.
+template <int D>
+__device__ __forceinline__ const __bf16* paged_row(const __bf16* pool, const PagedKV& pk, int b, int kvh,
+                                                   int hkv, int tok, int tok_last) {
+  const int t = min(tok, tok_last);
+  int pid = pk.table[(size_t)b * pk.max_pages + (t >> pk.page_log2)];
+  pid = min(max(pid, 0), pk.num_pages - 1);
+  const size_t row = ((((size_t)pid * hkv + kvh) << pk.page_log2) | (size_t)(t & ((1 << pk.page_log2) - 1)));
+  return pool + row * D;
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile_paged(DecodeTile<D>& t, const __bf16* kpool, const __bf16* vpool,
+                                                const PagedKV& pk, int b, int kvh, int hkv, int tok0,
+                                                int tok_last, int lane) {
+  constexpr int LPR = D / 8;
+  constexpr int RPI = 64 / LPR;
+  const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    const bf16x8* row = reinterpret_cast<const bf16x8*>(
+        paged_row<D>(kpool, pk, b, kvh, hkv, tok0 + n + 16 * bi, tok_last) + 8 * j);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) t.k[bi][kk] = __builtin_nontemporal_load(row + 4 * kk);
+  }
+#pragma unroll
+  for (int i = 0; i < kDecodeWaveTile * D / 8 / 64; ++i)
+    t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(
+        paged_row<D>(vpool, pk, b, kvh, hkv, tok0 + lane / LPR + RPI * i, tok_last) + 8 * (lane % LPR)));
+}
+
 #ifndef GQA_DECODE_WAVES_PER_EU
 #define GQA_DECODE_WAVES_PER_EU 3
 #endif
 
-template <int D>
+template <int D, bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA_DECODE_WAVES_PER_EU)))
 void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                        const __bf16* __restrict__ vc, const int32_t* __restrict__ lens,
                        float* __restrict__ out, float* __restrict__ part_o,
                        float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
-                       int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2) {
+                       int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2,
+                       PagedKV pk) {
   constexpr int KSTEPS = D / 32;          // QK^T MFMA steps over the head dim
   constexpr int DBLK = D / 16;            // PV MFMA blocks over the head dim
   constexpr int PITCH = DecodeBf16Smem<D>::kPitch;
@@ -281,7 +317,7 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
           if (n >= nh) qb[kk] = bf16x8{};
         }
       }
-      const size_t seg_off = (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D;
+      const size_t seg_off = kPaged ? 0 : (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + seg_off, nt * D * 2);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + seg_off, nt * D * 2);
 
@@ -293,7 +329,10 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
 
       for (int tok = w * kDecodeWaveTile; tok < nt; tok += STRIDE) {
         DecodeTile<D> tl;
-        load_tile<D>(tl, rk, rv, k_off, v_off, tok * D * 2);
+        if (kPaged)
+          load_tile_paged<D>(tl, kc, vc, pk, u.b, kvh, hkv, t0 + tok, t0 + nt - 1, lane);
+        else
+          load_tile<D>(tl, rk, rv, k_off, v_off, tok * D * 2);
         f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -588,7 +627,7 @@ DecodeWorkspace decode_workspace_layout(const DecodeShape& s) {
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
                                float* out, char* workspace, const DecodeShape& s,
-                               hipStream_t stream) {
+                               hipStream_t stream, const PagedKV& paged) {
   const int g = s.hq / s.hkv;
   const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
   const DecodeWorkspace wl = decode_workspace_layout(s);
@@ -602,12 +641,20 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
     auto qp = static_cast<const __bf16*>(q);
     auto kp = static_cast<const __bf16*>(k);
     auto vp = static_cast<const __bf16*>(v);
-    if (s.d == 128)
-      hipLaunchKernelGGL(decode_split_bf16<128>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
-    else
-      hipLaunchKernelGGL(decode_split_bf16<64>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
+    if (paged.table != nullptr) {
+      if (s.d == 128)
+        hipLaunchKernelGGL((decode_split_bf16<128, true>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                           plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+      else
+        hipLaunchKernelGGL((decode_split_bf16<64, true>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                           plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+    } else if (s.d == 128) {
+      hipLaunchKernelGGL((decode_split_bf16<128, false>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+    } else {
+      hipLaunchKernelGGL((decode_split_bf16<64, false>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
+                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+    }
   } else {
     auto qp = static_cast<const float*>(q);
     auto kp = static_cast<const float*>(k);

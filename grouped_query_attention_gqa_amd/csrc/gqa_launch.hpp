@@ -41,9 +41,17 @@ struct DecodeWorkspace {
 
 DecodeWorkspace decode_workspace_layout(const DecodeShape& s);
 
+// K/V held in a pool of pages [num_pages, Hkv, page_size, d]; table[b, i]
+// names the page of tokens i*page_size .. (i+1)*page_size-1 of sequence b.
+// A null table means the contiguous cache [batch, Hkv, tcap, d].
+struct PagedKV {
+  const int32_t* table;
+  int max_pages, num_pages, page_log2;
+};
+
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
                                float* out, char* workspace, const DecodeShape& s,
-                               hipStream_t stream);
+                               hipStream_t stream, const PagedKV& paged = PagedKV{nullptr, 0, 0, 0});
 
 hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
                                const DecodeShape& s, hipStream_t stream);

@@ -147,6 +147,52 @@ int32_t gqa_decode_merge(const int32_t* seq_lens, float* out, int32_t batch,
                          const void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * One decode step over a paged KV cache: the same attention as gqa_decode,
+ * with the cache stored in a shared pool of fixed-size pages addressed
+ * through a block table (deepconcepts.dev, "Grouped-Query Attention",
+ * section "Checking it on a real system": paged attention changes how the
+ * cache bytes are stored, not what attention computes; lihaoran.work,
+ * "Check the actual deployment": it acts on cache organisation, GQA on
+ * sharing structure).
+ *
+ *   k_pages, v_pages  [num_pages, num_kv_heads, page_size, head_dim] bf16
+ *   block_table       [batch, max_pages_per_seq] int32, device memory:
+ *                     entry [b, i] is the page holding tokens
+ *                     i*page_size .. (i+1)*page_size - 1 of sequence b.
+ *                     Only entries covering tokens below seq_lens[b] are
+ *                     read; an entry outside [0, num_pages) is clamped into
+ *                     the pool (wrong output, never an out-of-bounds read).
+ *   page_size         a power of two, 1 .. 65536
+ *   seq_lens          as for gqa_decode, clamped to [0, max_pages_per_seq *
+ *                     page_size]
+ *   workspace         at least what gqa_decode_plan reports for
+ *                     max_seq_len = max_pages_per_seq * page_size
+ *   dtype             GQA_BF16 only; head_dim 64 or 128
+ * Other arguments as for gqa_decode (the two stages run on the same stream).
+ */
+int32_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens, float* out,
+                         int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t page_size, int32_t num_pages,
+                         int32_t max_pages_per_seq, float scale, int32_t dtype,
+                         int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                         void* stream);
+
+/*
+ * First stage of gqa_decode_paged (the kernel that reads the pages), with the
+ * same outputs and workspace contents as gqa_decode_split; gqa_decode_merge
+ * with max_seq_len = max_pages_per_seq * page_size completes it.  Arguments
+ * as for gqa_decode_paged.
+ */
+int32_t gqa_decode_paged_split(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, float* out,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t page_size, int32_t num_pages,
+                               int32_t max_pages_per_seq, float scale, int32_t dtype,
+                               int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/*
  * Causal GQA over a whole prompt (prefill): query row i of head h attends to
  * keys 0..i of KV head h / g (lower-triangular mask broadcast over the
  * group; anrans.github.io, "Kernels do not need to copy the KV heads").
