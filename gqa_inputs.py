@@ -261,3 +261,70 @@ def make_paged(inp: DecodeInputs, page_size: int, spare_pages: int = 7, seed: in
             k_pages[pid, :, :hi - lo] = inp.k_cache[b, :, lo:hi]
             v_pages[pid, :, :hi - lo] = inp.v_cache[b, :, lo:hi]
     return PagedInputs(cfg, inp.q, k_pages, v_pages, table, inp.seq_lens, page_size)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache (storage format only; no attention arithmetic)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def _e4m3_positive_grid() -> np.ndarray:
+    """Values of the 127 non-negative finite E4M3 codes 0x00..0x7E, indexed by
+    code: exponent field e (bias 7), mantissa m (3 bits); e = 0 is subnormal."""
+    codes = np.arange(0x7F)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite values to OCP E4M3 (nearest, ties to even mantissa),
+    saturating at +-448; returns uint8 codes.  Never produces NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    grid = _e4m3_positive_grid()
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """Decode inputs with an E4M3 cache and one float32 scale per KV head for
+    K and for V: stored value * scale[kv head] is the cache value."""
+    cfg: DecodeConfig
+    q: np.ndarray          # [B, Hq, d] bf16 bits
+    k_cache: np.ndarray    # [B, Hkv, T_cap, d] uint8 E4M3 codes
+    v_cache: np.ndarray
+    k_scale: np.ndarray    # [Hkv] float32
+    v_scale: np.ndarray
+    seq_lens: np.ndarray
+
+
+def make_fp8(inp: DecodeInputs) -> Fp8Inputs:
+    """Quantise a bf16 decode cache per KV head: scale = max |x| / 448 over the
+    head's live tokens (amax scaling), codes = E4M3(x / scale).  Slots past a
+    sequence's length hold the NaN code 0x7F."""
+    assert inp.cfg.dtype == "bf16"
+    B, Hkv, T, d = inp.k_cache.shape
+    out = []
+    for cache in (inp.k_cache, inp.v_cache):
+        scales = np.empty(Hkv, dtype=np.float32)
+        codes = np.empty((B, Hkv, T, d), dtype=np.uint8)
+        for kv in range(Hkv):
+            amax = 0.0
+            for b in range(B):
+                t = int(inp.seq_lens[b])
+                if t:
+                    amax = max(amax, float(np.max(np.abs(bf16_bits_to_f32(cache[b, kv, :t])))))
+            scales[kv] = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+            for b in range(B):
+                codes[b, kv] = f32_to_e4m3_bits(bf16_bits_to_f32(cache[b, kv]).astype(np.float64)
+                                                / np.float64(scales[kv]))
+                codes[b, kv, int(inp.seq_lens[b]):] = 0x7F
+        out += [codes, scales]
+    return Fp8Inputs(inp.cfg, inp.q, out[0], out[2], out[1], out[3], inp.seq_lens)

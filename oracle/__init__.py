@@ -10,7 +10,8 @@ heads explicitly repeated along the query-head axis, in float64:
 
 * ``attention``   decode and causal prefill outputs (and log-sum-exp);
 * ``kv_math``     the closed forms for KV-cache bytes and decode FLOPs;
-* ``paged``       decode over a paged KV cache (gather, then the plain definition).
+* ``paged``       decode over a paged KV cache (gather, then the plain definition);
+* ``fp8``         decode over an E4M3 cache with per-KV-head scales (dequantise, then decode).
 
 Every function cites the passage of the source pages it follows.  The oracle
 is pinned by tests/test_oracle_pins.py against values the pages print, closed
@@ -28,6 +29,7 @@ from .attention import (  # noqa: F401
     prefill_causal_rows,
 )
 from .paged import gather_pages, decode_paged  # noqa: F401
+from .fp8 import e4m3_value, dequantize, decode_fp8  # noqa: F401
 from .kv_math import (  # noqa: F401
     kv_cache_bytes,
     kv_bytes_per_token,

@@ -78,3 +78,14 @@ def brute_decode_paged(q, k_pages, v_pages, block_table, seq_lens, page_size, sc
             rows.append(_attend(list(q[b][h]), keys, vals, scale) if T else [0.0] * len(q[b][h]))
         out.append(rows)
     return out
+
+
+def e4m3_scalar(code):
+    """One OCP E4M3 code as a Python float (math.ldexp on the bit fields)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0xF and m == 7:
+        return math.nan
+    if e == 0:
+        return sign * math.ldexp(m, -9)
+    return sign * math.ldexp(8 + m, e - 10)
