@@ -15,7 +15,8 @@ repeated steps.  Kernel durations come from HIP events on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
   python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|
-                  paged-llama3-8b|paged-wide-group] [--page-size P] [--no-cpu-baseline]
+                  paged-llama3-8b|paged-wide-group|fp8-llama3-8b|fp8-wide-group|fp8-mqa-128k]
+                  [--page-size P] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -165,7 +166,7 @@ def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
     return out
 
 
-def cpu_baseline_decode(inp, budget_s: float, pg=None, max_passes: int = 50):
+def cpu_baseline_decode(inp, budget_s: float, pg=None, fq=None, max_passes: int = 50):
     """Time the float64 oracle on the host, one whole sequence of the workload
     per call, cycling over the batch until about `budget_s` seconds of oracle
     time have been spent (input conversion to float64 is not timed).  For a
@@ -182,7 +183,11 @@ def cpu_baseline_decode(inp, budget_s: float, pg=None, max_passes: int = 50):
         while t_used < budget_s and calls < max_passes * cfg.batch:
             b = calls % cfg.batch
             q = gi.to_f64(inp.q[b:b + 1], cfg.dtype)
-            if pg is None:
+            if fq is not None:
+                t0 = time.perf_counter()
+                oracle.decode_fp8(q, fq.k_cache[b:b + 1], fq.v_cache[b:b + 1], fq.k_scale, fq.v_scale,
+                                  inp.seq_lens[b:b + 1], cfg.scale)
+            elif pg is None:
                 kf = gi.to_f64(inp.k_cache[b:b + 1], cfg.dtype)
                 vf = gi.to_f64(inp.v_cache[b:b + 1], cfg.dtype)
                 t0 = time.perf_counter()
@@ -197,13 +202,14 @@ def cpu_baseline_decode(inp, budget_s: float, pg=None, max_passes: int = 50):
                 oracle.decode_paged(q, kf, vf, table, inp.seq_lens[b:b + 1], pg.page_size, cfg.scale)
             t_used += time.perf_counter() - t0
             calls += 1
-            bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim, elem)
-    what = "decode_paged" if pg is not None else "decode"
+            bytes_done += decode_kv_bytes(inp.seq_lens[b:b + 1], cfg.num_kv_heads, cfg.head_dim,
+                                          1 if fq is not None else elem)
+    what = "decode_paged" if pg is not None else "decode_fp8" if fq is not None else "decode"
     return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle",
             "sample": f"{calls} single-sequence oracle.{what} calls cycling over the {cfg.batch} sequences of "
                       f"the same workload ({calls / cfg.batch:.2f} passes; float64 numpy, explicit K/V repeat), "
-                      f"{t_used:.1f} s of oracle time; value = K/V bytes of the bf16 cache / oracle time"}
+                      f"{t_used:.1f} s of oracle time; value = K/V bytes of the cache / oracle time"}
 
 
 def main():
@@ -212,7 +218,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b",
-                    choices=["llama3-8b", "wide-group", "mqa-128k", "paged-llama3-8b", "paged-wide-group"])
+                    choices=["llama3-8b", "wide-group", "mqa-128k", "paged-llama3-8b", "paged-wide-group",
+                             "fp8-llama3-8b", "fp8-wide-group", "fp8-mqa-128k"])
     ap.add_argument("--page-size", type=int, default=16, help="tokens per page for the paged-* workloads")
     ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/counters.json from two rocprofv3 --pmc counter CSVs and exit")
@@ -251,10 +258,11 @@ def main():
     torch.cuda.set_device(0)
 
     paged = args.workload.startswith("paged-")
-    cfg = gi.CONFIGS[args.workload[len("paged-"):] if paged else args.workload]
+    fp8 = args.workload.startswith("fp8-")
+    cfg = gi.CONFIGS[args.workload.split("-", 1)[1] if (paged or fp8) else args.workload]
     inp = gi.make_decode(cfg)
-    elem = 2 if cfg.dtype == "bf16" else 4
-    dt = gqa.GQA_BF16 if cfg.dtype == "bf16" else gqa.GQA_F32
+    elem = 1 if fp8 else (2 if cfg.dtype == "bf16" else 4)
+    dt = gqa.GQA_FP8_E4M3 if fp8 else (gqa.GQA_BF16 if cfg.dtype == "bf16" else gqa.GQA_F32)
     B, Hq, Hkv, d, T = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.max_seq_len
     kv_bytes = decode_kv_bytes(inp.seq_lens, Hkv, d, elem)
     alloc_kv = 2 * B * Hkv * T * d * elem
@@ -267,8 +275,14 @@ def main():
 
     q = to_dev(inp.q)
     lens = torch.from_numpy(inp.seq_lens).cuda()
-    pg = None
-    if paged:
+    pg = fq = None
+    if fp8:
+        # the same cache as E4M3 codes with per-KV-head scales
+        fq = gi.make_fp8(inp)
+        inp.k_cache = inp.v_cache = None
+        k0, v0 = torch.from_numpy(fq.k_cache).cuda(), torch.from_numpy(fq.v_cache).cuda()
+        k_scale, v_scale = torch.from_numpy(fq.k_scale).cuda(), torch.from_numpy(fq.v_scale).cuda()
+    elif paged:
         # the same cache scattered into a permuted pool of pages
         pg = gi.make_paged(inp, page_size=args.page_size)
         inp.k_cache = inp.v_cache = None
@@ -284,7 +298,10 @@ def main():
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
 
     def step(i):
-        if paged:
+        if fp8:
+            gqa.gqa_decode_fp8(q, ks[i % rot], vs[i % rot], k_scale, v_scale, lens, scale=cfg.scale, out=out,
+                               workspace=ws, split_tokens=args.split_tokens)
+        elif paged:
             gqa.gqa_decode_paged(q, ks[i % rot], vs[i % rot], table, lens, scale=cfg.scale, out=out,
                                  workspace=ws, split_tokens=args.split_tokens)
         else:
@@ -292,7 +309,10 @@ def main():
                            split_tokens=args.split_tokens)
 
     def split_only(i):
-        if paged:
+        if fp8:
+            gqa.gqa_decode_fp8(q, ks[i % rot], vs[i % rot], k_scale, v_scale, lens, scale=cfg.scale, out=out,
+                               workspace=ws, split_tokens=args.split_tokens, stage="split")
+        elif paged:
             gqa.gqa_decode_paged(q, ks[i % rot], vs[i % rot], table, lens, scale=cfg.scale, out=out,
                                  workspace=ws, split_tokens=args.split_tokens, stage="split")
         else:
@@ -309,6 +329,8 @@ def main():
     ms_split = event_time_ms(split_only, args.steps, torch)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     split_bytes = decode_split_bytes(inp.seq_lens, Hq, Hkv, d, elem)
+    if fp8:   # q is bf16 (2 B per element) and there are 2 * Hkv float scales
+        split_bytes += B * Hq * d * (2 - elem) + 8 * Hkv
     if paged:   # plus one read of each block-table entry in use
         split_bytes += 4 * int(np.sum(-(-inp.seq_lens.astype(np.int64) // args.page_size)))
     achieved = split_bytes / (ms_split * 1e-3) / 1e9
@@ -325,9 +347,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8-e4m3 cache, bf16 compute" if fp8 else cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": (f"paged (page {args.page_size}) " if paged else "") + gi.describe(cfg),
+        "config": {"workload": (f"paged (page {args.page_size}) " if paged else "FP8 E4M3 cache, " if fp8 else "")
+                   + gi.describe(cfg),
                    "global_batch": B, "seq_len": cfg.max_seq_len,
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
                    "range_tokens": plan.range_tokens or "auto", "workgroups": plan.workgroups,
@@ -335,8 +358,8 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "decode_tflops": round(decode_flops(inp.seq_lens, Hq, d) / (ms_step * 1e-3) / 1e12, 3),
-        "roofline": {"kernel": ("decode_split_bf16 (paged)" if paged else "decode_split_bf16")
-                     if cfg.dtype == "bf16" else "decode_split_f32",
+        "roofline": {"kernel": ("decode_split_bf16 (paged)" if paged else "decode_split_bf16 (E4M3 cache)"
+                                if fp8 else "decode_split_bf16") if cfg.dtype == "bf16" else "decode_split_f32",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": split_bytes,
@@ -381,7 +404,7 @@ def main():
         torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget, pg)
+        result["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget, pg, fq)
 
     print(json.dumps(result), flush=True)
 

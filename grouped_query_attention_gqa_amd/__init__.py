@@ -30,6 +30,7 @@ __all__ = [
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GQA_F32, GQA_BF16 = 0, 1
+GQA_FP8_E4M3 = 2   # bf16 q with an E4M3-coded cache and per-KV-head scales
 _STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
            4: "GQA_ERR_WORKSPACE", 5: "GQA_ERR_HIP", 6: "GQA_ERR_ALIGN"}
 
@@ -82,6 +83,10 @@ def load_library():
                                      P, I64, P]
     lib.gqa_decode_paged_split.restype = I32
     lib.gqa_decode_paged_split.argtypes = lib.gqa_decode_paged.argtypes
+    lib.gqa_decode_fp8.restype = I32
+    lib.gqa_decode_fp8.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, I64, P]
+    lib.gqa_decode_fp8_split.restype = I32
+    lib.gqa_decode_fp8_split.argtypes = lib.gqa_decode_fp8.argtypes
     lib.gqa_prefill_causal.restype = I32
     lib.gqa_prefill_causal.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P]
     _lib = lib
@@ -220,6 +225,42 @@ def gqa_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tens
     _check("gqa_decode_paged" if stage == "both" else "gqa_decode_paged_split", fn(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d,
         page_size, num_pages, max_pages, scale, dt, split_tokens, _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def gqa_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                   v_scale: torch.Tensor, seq_lens: torch.Tensor, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   split_tokens: int = 0, stage: str = "both") -> torch.Tensor:
+    """One GQA decode step over an E4M3 cache; returns out [B, Hq, d] float32.
+
+    q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, T_cap, d] uint8 codes;
+    k_scale, v_scale [Hkv] float32 (see gqa.h).  stage="split" runs only
+    gqa_decode_fp8_split (complete it with gqa_decode_merge, dtype
+    GQA_FP8_E4M3)."""
+    _require(q.dim() == 3 and q.dtype == torch.bfloat16, "q must be bf16 [B,Hq,d]")
+    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape and k_cache.dtype == torch.uint8
+             and v_cache.dtype == torch.uint8, "k_cache/v_cache must be uint8 [B,Hkv,T_cap,d] codes")
+    B, Hq, d = q.shape
+    B2, Hkv, tcap, d2 = k_cache.shape
+    _require(B == B2 and d == d2, "q and cache disagree on batch or head_dim")
+    _require(k_scale.dtype == torch.float32 and v_scale.dtype == torch.float32 and k_scale.shape == (Hkv,)
+             and v_scale.shape == (Hkv,), "k_scale/v_scale must be float32 [Hkv]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    dev = _on_gpu(q, k_cache, v_cache, k_scale, v_scale, seq_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    plan = gqa_decode_plan(B, Hq, Hkv, d, tcap, GQA_FP8_E4M3, split_tokens)
+    ws = _workspace(workspace, plan, dev)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, d), "out must be float32 [B,Hq,d]")
+    _on_gpu(q, out)
+    _require(stage in ("both", "split"), "stage must be 'both' or 'split'")
+    lib = load_library()
+    fn, name = (lib.gqa_decode_fp8, "gqa_decode_fp8") if stage == "both" else \
+        (lib.gqa_decode_fp8_split, "gqa_decode_fp8_split")
+    _check(name, fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+                    _ptr(out), B, Hq, Hkv, d, tcap, scale, split_tokens, _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
 

@@ -27,7 +27,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int32_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
   if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return GQA_ERR_SHAPE;
   if (d != 64 && d != 128) return GQA_ERR_UNSUPPORTED;
-  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_FP8_E4M3) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
@@ -133,6 +133,7 @@ int32_t gqa_decode_split(const void* q, const void* k_cache, const void* v_cache
                          float scale, int32_t dtype, int32_t split_tokens, void* workspace,
                          int64_t workspace_bytes, void* stream) {
   if (!out) return GQA_ERR_NULL;
+  if (dtype == GQA_FP8_E4M3) return GQA_ERR_UNSUPPORTED;   // needs the scales: gqa_decode_fp8_split
   gqa::DecodeShape s;
   gqa::DecodeWorkspace ws;
   const int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch,
@@ -167,6 +168,7 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                    int32_t dtype, int32_t split_tokens, void* workspace, int64_t workspace_bytes,
                    void* stream) {
   if (!out) return GQA_ERR_NULL;
+  if (dtype == GQA_FP8_E4M3) return GQA_ERR_UNSUPPORTED;   // needs the scales: gqa_decode_fp8
   gqa::DecodeShape s;
   gqa::DecodeWorkspace ws;
   int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch,
@@ -242,6 +244,44 @@ int32_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages
   st = hip_status(gqa::launch_decode_split(q, k_pages, v_pages, seq_lens, out, base, s, hs, pk));
   if (st != GQA_OK) return st;
   return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
+}
+
+static int32_t fp8_run(bool merge, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* seq_lens, float* out,
+                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_seq_len, float scale, int32_t split_tokens, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  if (!out || !k_scale || !v_scale) return GQA_ERR_NULL;
+  gqa::DecodeShape s;
+  gqa::DecodeWorkspace ws;
+  int32_t st = decode_prepare(q, k_cache, v_cache, seq_lens, workspace, workspace_bytes, batch, num_q_heads,
+                              num_kv_heads, head_dim, max_seq_len, scale, GQA_FP8_E4M3, split_tokens, &s, &ws);
+  if (st != GQA_OK) return st;
+  if (!aligned(out, 16) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return GQA_ERR_ALIGN;
+  char* base = static_cast<char*>(workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, out, base, s, hs,
+                                           gqa::PagedKV{nullptr, 0, 0, 0}, k_scale, v_scale));
+  if (st != GQA_OK || !merge) return st;
+  return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
+}
+
+int32_t gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                       const float* v_scale, const int32_t* seq_lens, float* out, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                       float scale, int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+  return fp8_run(true, q, k_cache, v_cache, k_scale, v_scale, seq_lens, out, batch, num_q_heads, num_kv_heads,
+                 head_dim, max_seq_len, scale, split_tokens, workspace, workspace_bytes, stream);
+}
+
+int32_t gqa_decode_fp8_split(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                             const float* v_scale, const int32_t* seq_lens, float* out, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_seq_len, float scale, int32_t split_tokens, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return fp8_run(false, q, k_cache, v_cache, k_scale, v_scale, seq_lens, out, batch, num_q_heads,
+                 num_kv_heads, head_dim, max_seq_len, scale, split_tokens, workspace, workspace_bytes, stream);
 }
 
 int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out, float* lse,

@@ -258,18 +258,69 @@ __device__ __forceinline__ void load_tile_paged(DecodeTile<D>& t, const __bf16* 
         paged_row<D>(vpool, pk, b, kvh, hkv, tok0 + lane / LPR + RPI * i, tok_last) + 8 * (lane % LPR)));
 }
 
+// FP8 (OCP E4M3) cache: 8 codes (two dwords, code i in byte i) to 8 bf16,
+// exactly (every E4M3 value is a bf16 value).  Each conversion result is used
+// as a whole 32-bit word: element extraction from the packed result is not
+// relied on.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(unsigned w0, unsigned w1) {
+  const u32x4 r = {__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// One wavefront's 32-token tile of an E4M3 cache, as loaded (16-byte chunks).
+// K: lane (row n, group j) holds the D/4 contiguous codes of rows n and n+16
+// starting at column j*D/4, so its MFMA k-slots for step kk are columns
+// j*D/4 + 8kk .. +7 (q is laid out the same way).  V: lane holds 16 codes of
+// row i*RPI8 + lane/LPR8 starting at column 16*(lane%LPR8).
+template <int D>
+struct DecodeTileF8 {
+  static constexpr int KCH = D / 64;          // 16-byte chunks per lane per K row
+  static constexpr int LPR8 = D / 16;         // lanes per V row
+  static constexpr int RPI8 = 64 / LPR8;      // V rows per load
+  static constexpr int VLOADS8 = kDecodeWaveTile / RPI8;
+  u32x4 k[2][KCH];
+  u32x4 v[VLOADS8];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile_f8(DecodeTileF8<D>& t, __amdgpu_buffer_rsrc_t rk,
+                                             __amdgpu_buffer_rsrc_t rv, int lane, int tile_bytes) {
+  using T = DecodeTileF8<D>;
+  const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int c = 0; c < T::KCH; ++c)
+      t.k[bi][c] = __builtin_bit_cast(u32x4, buffer_load_bf16x8<kCacheStream>(
+          rk, tile_bytes + (n + 16 * bi) * D + j * (D / 4) + 16 * c, 0));
+#pragma unroll
+  for (int i = 0; i < T::VLOADS8; ++i)
+    t.v[i] = __builtin_bit_cast(u32x4, buffer_load_bf16x8<kCacheStream>(
+        rv, tile_bytes + (i * T::RPI8 + lane / T::LPR8) * D + 16 * (lane % T::LPR8), 0));
+}
+
 #ifndef GQA_DECODE_WAVES_PER_EU
 #define GQA_DECODE_WAVES_PER_EU 3
 #endif
 
-template <int D, bool kPaged>
+// kPaged: K/V in a page pool addressed through a block table.  kFp8: K/V
+// stored as E4M3 codes with one float scale per KV head (k_scale folds into
+// the softmax scale, v_scale multiplies the normalised output).
+template <int D, bool kPaged, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA_DECODE_WAVES_PER_EU)))
-void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
-                       const __bf16* __restrict__ vc, const int32_t* __restrict__ lens,
+void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kcv,
+                       const void* __restrict__ vcv, const int32_t* __restrict__ lens,
                        float* __restrict__ out, float* __restrict__ part_o,
                        float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
                        int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2,
-                       PagedKV pk) {
+                       PagedKV pk, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  static_assert(!(kPaged && kFp8), "paged FP8 caches are not supported");
+  const __bf16* kc = static_cast<const __bf16*>(kcv);
+  const __bf16* vc = static_cast<const __bf16*>(vcv);
+  constexpr int ELEM = kFp8 ? 1 : 2;      // bytes per cached element
   constexpr int KSTEPS = D / 32;          // QK^T MFMA steps over the head dim
   constexpr int DBLK = D / 16;            // PV MFMA blocks over the head dim
   constexpr int PITCH = DecodeBf16Smem<D>::kPitch;
@@ -307,19 +358,22 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
       const int h_first = kvh * g + hb * kDecodeHeadBlock;
       const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
 
-      // Q^T as the B operand: lane holds q[h_first+n][8j + 32kk .. +7].
+      // Q^T as the B operand: lane holds q[h_first+n][8j + 32kk .. +7]
+      // (for an E4M3 cache: q[..][j*D/4 + 8kk .. +7], the K slot order).
       bf16x8 qb[KSTEPS];
       {
         const __bf16* qrow = q + ((size_t)u.b * hq + h_first + min(n, nh - 1)) * D;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          qb[kk] = load_bf16x8(qrow + 8 * j + 32 * kk);
+          qb[kk] = load_bf16x8(qrow + (kFp8 ? j * (D / 4) + 8 * kk : 8 * j + 32 * kk));
           if (n >= nh) qb[kk] = bf16x8{};
         }
       }
-      const size_t seg_off = kPaged ? 0 : (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + seg_off, nt * D * 2);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + seg_off, nt * D * 2);
+      const size_t seg_off = kPaged ? 0 : (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D * ELEM;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const char*>(kcv) + seg_off, nt * D * ELEM);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const char*>(vcv) + seg_off, nt * D * ELEM);
+      const float sl2 = kFp8 ? scale_log2 * k_scale[kvh] : scale_log2;
+      const float vsc = kFp8 ? v_scale[kvh] : 1.f;
 
       float m = -INFINITY;   // running max of head n (log2 domain), same in all 4 lane groups
       float lsum = 0.f;      // this lane's share of the running denominator of head n
@@ -329,10 +383,19 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
 
       for (int tok = w * kDecodeWaveTile; tok < nt; tok += STRIDE) {
         DecodeTile<D> tl;
-        if (kPaged)
+        DecodeTileF8<D> tf;
+        if (kFp8) {
+          load_tile_f8<D>(tf, rk, rv, lane, tok * D);
+#pragma unroll
+          for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+              tl.k[bi][kk] = e4m3x8_to_bf16(tf.k[bi][kk >> 1][2 * (kk & 1)], tf.k[bi][kk >> 1][2 * (kk & 1) + 1]);
+        } else if (kPaged) {
           load_tile_paged<D>(tl, kc, vc, pk, u.b, kvh, hkv, t0 + tok, t0 + nt - 1, lane);
-        else
+        } else {
           load_tile<D>(tl, rk, rv, k_off, v_off, tok * D * 2);
+        }
         f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -345,7 +408,7 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tt = tok + 16 * (e >> 2) + 4 * j + (e & 3);
-          s2[e] = tt < nt ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+          s2[e] = tt < nt ? sc[e >> 2][e & 3] * sl2 : -INFINITY;
           mx = fmaxf(mx, s2[e]);
         }
         mx = fmaxf(mx, shfl_xor(mx, 16));
@@ -366,9 +429,19 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
         for (int i = 0; i < DBLK; ++i) acc[i] *= alpha;
 
         wave_sync();   // the previous tile's transposed reads are done
+        if (kFp8) {
+          using TF = DecodeTileF8<D>;
 #pragma unroll
-        for (int i = 0; i < VLOADS; ++i)
-          store_bf16x8(vt + (i * RPI + lane / LPR) * PITCH + 8 * (lane % LPR), tl.v[i]);
+          for (int i = 0; i < TF::VLOADS8; ++i) {
+            __bf16* dst = vt + (i * TF::RPI8 + lane / TF::LPR8) * PITCH + 16 * (lane % TF::LPR8);
+            store_bf16x8(dst, e4m3x8_to_bf16(tf.v[i][0], tf.v[i][1]));
+            store_bf16x8(dst + 8, e4m3x8_to_bf16(tf.v[i][2], tf.v[i][3]));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < VLOADS; ++i)
+            store_bf16x8(vt + (i * RPI + lane / LPR) * PITCH + 8 * (lane % LPR), tl.v[i]);
+        }
         wave_sync();
         // V^T as the A operand: k-slots 0..3 are tokens 4j..4j+3 and slots
         // 4..7 are tokens 16+4j..16+4j+3, matching the P^T slots in pb.
@@ -412,9 +485,9 @@ void decode_split_bf16(const __bf16* __restrict__ q, const __bf16* __restrict__ 
           Os += co[(ww * kDecodeHeadBlock + h) * OP + dd] * wt;
         }
         if (nseg == 1) {
-          out[((size_t)u.b * hq + h_first + h) * D + dd] = Os / Ls;
+          out[((size_t)u.b * hq + h_first + h) * D + dd] = Os / Ls * vsc;
         } else {
-          part_o[(slot * kDecodeHeadBlock + h) * D + dd] = Os / Ls;
+          part_o[(slot * kDecodeHeadBlock + h) * D + dd] = Os / Ls * vsc;
           if (dd == 0) part_lse[slot * kDecodeHeadBlock + h] = M + __log2f(Ls);
         }
       }
@@ -627,7 +700,8 @@ DecodeWorkspace decode_workspace_layout(const DecodeShape& s) {
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
                                float* out, char* workspace, const DecodeShape& s,
-                               hipStream_t stream, const PagedKV& paged) {
+                               hipStream_t stream, const PagedKV& paged, const float* k_scale,
+                               const float* v_scale) {
   const int g = s.hq / s.hkv;
   const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
   const DecodeWorkspace wl = decode_workspace_layout(s);
@@ -637,24 +711,22 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
   const dim3 grid(s.grid);
   const dim3 block(kThreads);
   const float sl2 = s.scale * kLog2e;
-  if (s.dtype == 1) {
+  if (s.dtype == 1 || s.dtype == 2) {
     auto qp = static_cast<const __bf16*>(q);
-    auto kp = static_cast<const __bf16*>(k);
-    auto vp = static_cast<const __bf16*>(v);
-    if (paged.table != nullptr) {
-      if (s.d == 128)
-        hipLaunchKernelGGL((decode_split_bf16<128, true>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                           plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
-      else
-        hipLaunchKernelGGL((decode_split_bf16<64, true>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                           plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
-    } else if (s.d == 128) {
-      hipLaunchKernelGGL((decode_split_bf16<128, false>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+#define GQA_SPLIT(DD, PG, F8)                                                                          \
+  hipLaunchKernelGGL((decode_split_bf16<DD, PG, F8>), grid, block, 0, stream, qp, k, v, lens, out, po, plse, \
+                     info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged, k_scale, v_scale)
+    if (s.dtype == 2) {
+      if (s.d == 128) GQA_SPLIT(128, false, true);
+      else GQA_SPLIT(64, false, true);
+    } else if (paged.table != nullptr) {
+      if (s.d == 128) GQA_SPLIT(128, true, false);
+      else GQA_SPLIT(64, true, false);
     } else {
-      hipLaunchKernelGGL((decode_split_bf16<64, false>), grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged);
+      if (s.d == 128) GQA_SPLIT(128, false, false);
+      else GQA_SPLIT(64, false, false);
     }
+#undef GQA_SPLIT
   } else {
     auto qp = static_cast<const float*>(q);
     auto kp = static_cast<const float*>(k);

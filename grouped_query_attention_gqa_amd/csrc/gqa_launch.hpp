@@ -29,7 +29,7 @@ struct DecodeShape {
   int grid;          // workgroups launched
   int64_t max_slots; // upper bound on partial slots (ranges + units)
   float scale;
-  int dtype;         // gqa_dtype
+  int dtype;         // gqa_dtype (GQA_FP8_E4M3: bf16 q with an E4M3 cache)
 };
 
 // Byte offsets of the workspace arrays: per-unit (first slot, segment
@@ -51,7 +51,8 @@ struct PagedKV {
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, const int32_t* lens,
                                float* out, char* workspace, const DecodeShape& s,
-                               hipStream_t stream, const PagedKV& paged = PagedKV{nullptr, 0, 0, 0});
+                               hipStream_t stream, const PagedKV& paged = PagedKV{nullptr, 0, 0, 0},
+                               const float* k_scale = nullptr, const float* v_scale = nullptr);
 
 hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
                                const DecodeShape& s, hipStream_t stream);

@@ -59,7 +59,10 @@ typedef enum gqa_status {
 
 typedef enum gqa_dtype {
   GQA_F32 = 0,  /* IEEE float32                          */
-  GQA_BF16 = 1  /* bfloat16 (upper half of a float32)     */
+  GQA_BF16 = 1, /* bfloat16 (upper half of a float32)     */
+  GQA_FP8_E4M3 = 2 /* bf16 q with a KV cache of OCP E4M3 codes and per-KV-head
+                      float32 scales (gqa_decode_fp8); valid for the plan,
+                      gqa_decode_fp8* and gqa_decode_merge */
 } gqa_dtype;
 
 /* Version of this ABI (GQA_ABI_VERSION). */
@@ -191,6 +194,41 @@ int32_t gqa_decode_paged_split(const void* q, const void* k_pages, const void* v
                                int32_t max_pages_per_seq, float scale, int32_t dtype,
                                int32_t split_tokens, void* workspace, int64_t workspace_bytes,
                                void* stream);
+
+/*
+ * One decode step over an FP8 KV cache (deepconcepts.dev, "Grouped-Query
+ * Attention", section "Checking it on a real system": quantising the cache
+ * halves its bytes again; anrans.github.io, "Other ways to shrink the KV
+ * cache": K and V stored in FP8).  The cache holds OCP E4M3 codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits); the value of a code of KV
+ * head kv is code_value * k_scale[kv] (K) or * v_scale[kv] (V).  Attention
+ * is then exactly that of gqa_decode over the decoded values.
+ *
+ *   q                 [batch, num_q_heads, head_dim] bf16
+ *   k_cache, v_cache  [batch, num_kv_heads, max_seq_len, head_dim] uint8 codes
+ *   k_scale, v_scale  [num_kv_heads] float32, device memory
+ *   workspace         at least what gqa_decode_plan reports with dtype
+ *                     GQA_FP8_E4M3
+ * Other arguments, limits and errors as for gqa_decode; head_dim 64 or 128.
+ * Codes of cached tokens are read as stored (NaN codes give NaN outputs);
+ * slots past seq_lens[b] are never read.
+ */
+int32_t gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                       float* out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_seq_len, float scale, int32_t split_tokens,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * First stage of gqa_decode_fp8 (the kernel that reads the cache); complete
+ * it with gqa_decode_merge (dtype GQA_FP8_E4M3).  Arguments as for
+ * gqa_decode_fp8.
+ */
+int32_t gqa_decode_fp8_split(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             float* out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_seq_len, float scale, int32_t split_tokens,
+                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Causal GQA over a whole prompt (prefill): query row i of head h attends to
