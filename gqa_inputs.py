@@ -18,7 +18,9 @@ Recipe: seeds 1001..1005 in the order listed above; ``SeedSequence(seed).spawn(4
 independent PCG64 streams for (lengths, Q, K, V) in that order; values are
 i.i.d. standard normal drawn as float32 and, for bf16 workloads, rounded to
 bfloat16 with round-to-nearest-even.  Cache slots past a sequence's length
-are filled with NaN so that any kernel reading them is caught.
+are filled with NaN so that any kernel reading them is caught.  The
+backward pass of a prefill workload also draws an upstream output gradient
+from a fifth child stream (``make_dout``).
 
 Head-major layouts: q ``[B, Hq, d]`` (decode) or ``[B, Hq, N, d]`` (prefill);
 k/v ``[B, Hkv, T_cap, d]`` (decode cache) or ``[B, Hkv, N, d]`` (prefill).
@@ -215,6 +217,15 @@ def small_prefill(batch: int, num_q_heads: int, num_kv_heads: int, seq_len: int,
     cfg = PrefillConfig(f"small-{seed}", "bf16", batch, num_q_heads, num_kv_heads,
                         head_dim, seq_len, seed)
     return make_prefill(cfg)
+
+
+def make_dout(cfg: PrefillConfig) -> np.ndarray:
+    """Upstream gradient of the prefill output, [B, Hq, N, d], for the
+    backward pass: i.i.d. standard normal from the fifth child stream of the
+    workload's seed (the first four, and hence q/k/v, are unchanged), stored
+    like q (bf16 bits for bf16 workloads)."""
+    r_do = np.random.Generator(np.random.PCG64(np.random.SeedSequence(cfg.seed).spawn(5)[4]))
+    return _normals(r_do, (cfg.batch, cfg.num_q_heads, cfg.seq_len, cfg.head_dim), cfg.dtype)
 
 
 # ---------------------------------------------------------------------------

@@ -11,7 +11,8 @@ heads explicitly repeated along the query-head axis, in float64:
 * ``attention``   decode and causal prefill outputs (and log-sum-exp);
 * ``kv_math``     the closed forms for KV-cache bytes and decode FLOPs;
 * ``paged``       decode over a paged KV cache (gather, then the plain definition);
-* ``fp8``         decode over an E4M3 cache with per-KV-head scales (dequantise, then decode).
+* ``fp8``         decode over an E4M3 cache with per-KV-head scales (dequantise, then decode);
+* ``backward``    gradients of causal prefill (repeat K/V, chain rule per head, sum back).
 
 Every function cites the passage of the source pages it follows.  The oracle
 is pinned by tests/test_oracle_pins.py against values the pages print, closed
@@ -30,6 +31,11 @@ from .attention import (  # noqa: F401
 )
 from .paged import gather_pages, decode_paged  # noqa: F401
 from .fp8 import e4m3_value, dequantize, decode_fp8  # noqa: F401
+from .backward import (  # noqa: F401
+    reduce_kv_heads,
+    prefill_causal_backward,
+    prefill_causal_backward_group,
+)
 from .kv_math import (  # noqa: F401
     kv_cache_bytes,
     kv_bytes_per_token,
