@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
     "gqa_decode_plan", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
-    "gqa_prefill_causal", "GQA_F32", "GQA_BF16",
+    "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
+    "GQA_F32", "GQA_BF16",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +90,10 @@ def load_library():
     lib.gqa_decode_fp8_split.argtypes = lib.gqa_decode_fp8.argtypes
     lib.gqa_prefill_causal.restype = I32
     lib.gqa_prefill_causal.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P]
+    lib.gqa_prefill_backward_workspace.restype = I32
+    lib.gqa_prefill_backward_workspace.argtypes = [I32] * 5 + [ctypes.POINTER(I64)]
+    lib.gqa_prefill_causal_backward.restype = I32
+    lib.gqa_prefill_causal_backward.argtypes = [P] * 9 + [I32] * 5 + [F32, I32, P, I64, P]
     _lib = lib
     return lib
 
@@ -317,3 +322,54 @@ def gqa_prefill_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check("gqa_prefill_causal", lib.gqa_prefill_causal(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale, dt, _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def gqa_prefill_backward_workspace(batch: int, num_q_heads: int, num_kv_heads: int, seq_len: int,
+                                   head_dim: int) -> int:
+    """Workspace bytes of ``gqa_prefill_causal_backward`` for this shape."""
+    lib = load_library()
+    nbytes = ctypes.c_int64()
+    _check("gqa_prefill_backward_workspace", lib.gqa_prefill_backward_workspace(
+        batch, num_q_heads, num_kv_heads, seq_len, head_dim, ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def gqa_prefill_causal_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                lse: torch.Tensor, dout: torch.Tensor, scale: Optional[float] = None,
+                                workspace: Optional[torch.Tensor] = None, grads=None):
+    """Gradients (dq, dk, dv) of causal GQA prefill, all float32 (see gqa.h).
+
+    ``out`` and ``lse`` are what ``gqa_prefill_causal`` returned for these
+    q, k, v and scale; ``dout`` [B, Hq, N, d] bf16 is the gradient of the
+    loss with respect to ``out``.  ``grads`` may supply the three output
+    tensors."""
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "expected 4-d q, k, v")
+    _require(k.shape == v.shape, "k and v shapes differ")
+    B, Hq, N, d = q.shape
+    B2, Hkv, N2, d2 = k.shape
+    _require(B == B2 and N == N2 and d == d2, "q and k/v disagree on batch, length or head_dim")
+    _require(q.dtype == k.dtype == v.dtype == dout.dtype, "q, k, v, dout must share a dtype")
+    _require(dout.shape == q.shape, "dout must have q's shape")
+    _require(out.dtype == torch.float32 and out.shape == q.shape, "out must be float32 [B,Hq,N,d]")
+    _require(lse.dtype == torch.float32 and lse.shape == (B, Hq, N), "lse must be float32 [B,Hq,N]")
+    dev = _on_gpu(q, k, v, out, lse, dout)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if grads is None:
+        grads = (torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev))
+    dq, dk, dv = grads
+    _require(dq.dtype == torch.float32 and dq.shape == q.shape, "dq must be float32 [B,Hq,N,d]")
+    _require(dk.dtype == torch.float32 and dk.shape == k.shape, "dk must be float32 [B,Hkv,N,d]")
+    _require(dv.dtype == torch.float32 and dv.shape == k.shape, "dv must be float32 [B,Hkv,N,d]")
+    _on_gpu(q, dq, dk, dv)
+    if workspace is None:
+        nbytes = gqa_prefill_backward_workspace(B, Hq, Hkv, N, d) if dt == GQA_BF16 else 256
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _on_gpu(q, workspace)
+    lib = load_library()
+    _check("gqa_prefill_causal_backward", lib.gqa_prefill_causal_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, Hq, Hkv, N, d, scale, dt, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dq, dk, dv

@@ -75,6 +75,28 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tca
   return GQA_OK;
 }
 
+// Shape rules of the causal prefill entry points (forward and backward).
+int32_t check_prefill(int32_t batch, int32_t hq, int32_t hkv, int32_t n, int32_t d, int32_t dtype) {
+  int32_t st = check_heads(batch, hq, hkv, d, dtype);
+  if (st != GQA_OK) return st;
+  if (n < 1) return GQA_ERR_SHAPE;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  const int64_t q_elems = (int64_t)batch * hq * (int64_t)n * d;
+  if (q_elems / d / n / hq != batch || q_elems > (INT64_MAX / 8)) return GQA_ERR_SHAPE;
+  // one head's rows are addressed with 32-bit buffer offsets
+  if ((int64_t)n * d * 4 > INT32_MAX) return GQA_ERR_SHAPE;
+  const int64_t g = hq / hkv;
+  const int64_t gw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int64_t tiles = (n + 128 / gw - 1) / (128 / gw);
+  if ((int64_t)batch * hkv * (g / gw) * tiles > INT32_MAX) return GQA_ERR_SHAPE;
+  return GQA_OK;
+}
+
+// The backward's workspace is D = rowsum(dout * out), one float per query row.
+int64_t backward_workspace_bytes(int32_t batch, int32_t hq, int32_t n) {
+  return ((int64_t)batch * hq * n * 4 + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,22 +311,41 @@ int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* o
                            int32_t seq_len, int32_t head_dim, float scale, int32_t dtype,
                            void* stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
-  int32_t st = check_heads(batch, num_q_heads, num_kv_heads, head_dim, dtype);
+  const int32_t st = check_prefill(batch, num_q_heads, num_kv_heads, seq_len, head_dim, dtype);
   if (st != GQA_OK) return st;
-  if (seq_len < 1) return GQA_ERR_SHAPE;
-  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
-  const int64_t q_elems = (int64_t)batch * num_q_heads * (int64_t)seq_len * head_dim;
-  if (q_elems / head_dim / seq_len / num_q_heads != batch || q_elems > (INT64_MAX / 8))
-    return GQA_ERR_SHAPE;
-  const int64_t g = num_q_heads / num_kv_heads;
-  const int64_t gw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
-  const int64_t tiles = (seq_len + 128 / gw - 1) / (128 / gw);
-  if ((int64_t)batch * num_kv_heads * (g / gw) * tiles > INT32_MAX) return GQA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       (lse && !aligned(lse, 4)))
     return GQA_ERR_ALIGN;
   gqa::PrefillShape s{batch, num_q_heads, num_kv_heads, seq_len, head_dim, scale};
   return hip_status(gqa::launch_prefill_causal(q, k, v, out, lse, s, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gqa_prefill_backward_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t seq_len, int32_t head_dim, int64_t* workspace_bytes_out) {
+  if (!workspace_bytes_out) return GQA_ERR_NULL;
+  const int32_t st = check_prefill(batch, num_q_heads, num_kv_heads, seq_len, head_dim, GQA_BF16);
+  if (st != GQA_OK) return st;
+  *workspace_bytes_out = backward_workspace_bytes(batch, num_q_heads, seq_len);
+  return GQA_OK;
+}
+
+int32_t gqa_prefill_causal_backward(const void* q, const void* k, const void* v, const float* out,
+                                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t seq_len, int32_t head_dim, float scale, int32_t dtype,
+                                    void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return GQA_ERR_NULL;
+  const int32_t st = check_prefill(batch, num_q_heads, num_kv_heads, seq_len, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (workspace_bytes < backward_workspace_bytes(batch, num_q_heads, seq_len)) return GQA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) ||
+      !aligned(lse, 4))
+    return GQA_ERR_ALIGN;
+  gqa::PrefillShape s{batch, num_q_heads, num_kv_heads, seq_len, head_dim, scale};
+  return hip_status(gqa::launch_prefill_backward(q, k, v, out, lse, dout, dq, dk, dv,
+                                                 static_cast<float*>(workspace), s,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -65,4 +65,11 @@ struct PrefillShape {
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, float* out,
                                  float* lse, const PrefillShape& s, hipStream_t stream);
 
+// Backward of causal prefill: dq, then (after it, on the same stream) dk and
+// dv; `delta` [batch, hq, n] receives rowsum(dout * out) from the first
+// kernel and is read by the second.
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* out,
+                                   const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                   float* delta, const PrefillShape& s, hipStream_t stream);
+
 }  // namespace gqa

@@ -31,44 +31,16 @@
 
 #include "gqa_device.hpp"
 #include "gqa_launch.hpp"
+#include "prefill_tiles.hpp"
 
 namespace gqa {
 
 namespace {
 
 constexpr int kRows = 128;   // query rows per workgroup
-constexpr int kBN = 64;      // keys per tile
+constexpr int kBN = tiles::kRows;   // keys per tile
 constexpr int kXcds = 8;
-constexpr int kPrefillThreads = 256;
-
-// Physical 16-byte chunk of logical chunk c in key row r: c ^ rot(r), with
-// rot a one-bit left rotation of r within the chunk-index width (a
-// bijection that is linear under XOR).
-template <int CPR>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int BITS = CPR == 16 ? 4 : 3;
-  const int x = r & (CPR - 1);
-  return c ^ (((x << 1) | (x >> (BITS - 1))) & (CPR - 1));
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Start the direct global-to-LDS loads of one K tile and one V tile (keys
-// t0 .. t0+63): the wave's lanes fill consecutive 16-byte chunks of its 1 KiB
-// block per instruction, each from the global offset src_off[i].
-template <int D, int LOADS>
-__device__ __forceinline__ void issue_tile(__bf16* kdst, __bf16* vdst, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, const int (&src_off)[LOADS],
-                                           int w, int t0) {
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int dst = (w * 64 + kPrefillThreads * i) * 8;   // wave's 1 KiB block, in bf16 units
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kdst + dst), 16,
-                                             t0 * D * 2 + src_off[i], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vdst + dst), 16,
-                                             t0 * D * 2 + src_off[i], 0, 0, 0);
-  }
-}
+constexpr int kPrefillThreads = tiles::kThreads;
 
 // Per-lane constants of a wavefront: its Q operands and the LDS element
 // offsets of its K and V operands within a tile.
@@ -112,8 +84,7 @@ __device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, 
   bf16x8 va[2][DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    va[0][db] = concat(lds_read_tr16(vs + ln.v_rd[0][db]),
-                       lds_read_tr16(vs + ln.v_rd[0][db] + 8 * D + ln.v_dx[0][db]));
+    va[0][db] = tiles::read_tr<D>(vs, ln.v_rd[0][db], ln.v_dx[0][db]);
   __builtin_amdgcn_sched_barrier(0);
 
   // sc[kb][r] = raw score of key t0 + 32*kb + 8*(r/4) + 4*j + r%4, query row
@@ -188,8 +159,7 @@ __device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, 
     if (c + 1 < 4) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        va[(c + 1) & 1][db] = concat(lds_read_tr16(vs + ln.v_rd[c + 1][db]),
-                                     lds_read_tr16(vs + ln.v_rd[c + 1][db] + 8 * D + ln.v_dx[c + 1][db]));
+        va[(c + 1) & 1][db] = tiles::read_tr<D>(vs, ln.v_rd[c + 1][db], ln.v_dx[c + 1][db]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -205,9 +175,7 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
                          int n_qtiles, int units, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;            // 16-byte chunks per key row
   constexpr int TILE = kBN * D;         // bf16 elements per K or V tile
-  constexpr int LOADS = kBN * CPR / kPrefillThreads;   // 16-byte loads per thread per tile
   __shared__ __align__(16) __bf16 k0s[TILE];
   __shared__ __align__(16) __bf16 v0s[TILE];
   __shared__ __align__(16) __bf16 k1s[TILE];
@@ -251,36 +219,18 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int key = 32 * kb + row;
-        ln.k_rd[kb][kk] = key * D + swz<CPR>(key, 2 * kk + j) * 8;
-      }
-    const int L = lane & 15;
-    const int dlo = 16 * ((lane >> 4) & 1);   // which 16 of the 32 A rows
+      for (int kk = 0; kk < KSTEPS; ++kk) ln.k_rd[kb][kk] = tiles::row_offset<D>(32 * kb + row, 2 * kk + j);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int key = 16 * c + 4 * j + (L >> 2);
-        const int col = 32 * db + dlo + 4 * (L & 3);
-        ln.v_rd[c][db] = key * D + swz<CPR>(key, col >> 3) * 8 + (col & 7);
-        ln.v_dx[c][db] = (swz<CPR>(key + 8, col >> 3) - swz<CPR>(key, col >> 3)) * 8;
-      }
+      for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, ln.v_rd[c][db], ln.v_dx[c][db]);
   }
 
   // K/V of this (sequence, KV head); rows >= n read as zeros.
   const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, n * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, n * D * 2);
-  // Thread tid fills physical chunks p = tid + 256*i of a tile (LDS byte
-  // 16*p); it loads the logical chunk that the swizzle places there.
-  int src_off[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = tid + kPrefillThreads * i;
-    const int key = p / CPR;
-    src_off[i] = key * D * 2 + swz<CPR>(key, p % CPR) * 16;
-  }
+  const tiles::TileFill<D> fill(tid);
 
   RowState<D> st;
   st.m = -INFINITY;
@@ -292,18 +242,18 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int wave_hi = min(n, pos0 + 32);   // keys this wavefront needs
   const int ntiles = (kv_hi + kBN - 1) / kBN;
 
-  issue_tile<D, LOADS>(k0s, v0s, rk, rv, src_off, w, 0);
+  fill.issue2(k0s, rk, v0s, rv, w, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
     // stage 0 holds tile it
-    if (it + 1 < ntiles) issue_tile<D, LOADS>(k1s, v1s, rk, rv, src_off, w, (it + 1) * kBN);
+    if (it + 1 < ntiles) fill.issue2(k1s, rk, v1s, rv, w, (it + 1) * kBN);
     if (it * kBN < wave_hi) attend_tile<D>(k0s, v0s, ln, st, it * kBN, pos0, pos, n, j, scale_log2);
     __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile have landed
     __syncthreads();                 // ... everyone's, and everyone is done with stage 0
     if (it + 1 >= ntiles) break;
     // stage 1 holds tile it + 1
-    if (it + 2 < ntiles) issue_tile<D, LOADS>(k0s, v0s, rk, rv, src_off, w, (it + 2) * kBN);
+    if (it + 2 < ntiles) fill.issue2(k0s, rk, v0s, rv, w, (it + 2) * kBN);
     if ((it + 1) * kBN < wave_hi)
       attend_tile<D>(k1s, v1s, ln, st, (it + 1) * kBN, pos0, pos, n, j, scale_log2);
     __builtin_amdgcn_s_waitcnt(0);

@@ -1,0 +1,421 @@
+// Causal GQA prefill backward on gfx950 bf16 matrix cores.
+//
+// Gradients of out_h = softmax(scale Q_h K^T, causal) V for every query head
+// h, with K and V shared by the g consecutive query heads of a group: a
+// shared K or V row collects gradient from every query head of its group
+// (study.greatitself.com, "Grouped-Query and Multi-Query Attention", section
+// "Share keys and values without confusing query-head identity", training
+// paragraph).  P is recomputed tile by tile from the forward's log-sum-exp,
+// P = exp(scale q.k - lse), and with the row term D_i = rowsum(dO_i * O_i)
+// (equal to rowsum(P_i * dP_i), the correction of the softmax Jacobian):
+//
+//   dV[kv] = sum over the group's heads of P^T dO
+//   dS     = P * (dO V^T - D)
+//   dQ     = scale dS K
+//   dK[kv] = scale * sum over the group's heads of dS^T Q
+//
+// Two kernels, no atomics, bitwise deterministic:
+//  * prefill_bwd_dq: a workgroup owns 128 query rows of one KV head's group
+//    (the forward's partition: Gw heads x 128/Gw positions), streams the K/V
+//    tiles of keys up to its diagonal through LDS and accumulates dQ^T in
+//    registers.  Its prologue forms D for its rows from out and dO and
+//    stores it for the second kernel.
+//  * prefill_bwd_dkdv: a workgroup owns 128 keys of one KV head (32 per
+//    wavefront, with K and V held in registers as MFMA operands) and
+//    streams, through double-buffered LDS, the Q/dO tiles of every query
+//    head of the group at every position from its first key on.  dK and dV
+//    of the KV head are summed over the g heads in registers: per-head
+//    gradients never reach memory and the shared K/V rows are never copied.
+//    Q tiles are visited from the last one down, so all workgroups of one
+//    KV head start on the same tile and move through Q/dO together, and
+//    workgroups are issued heaviest (first keys) first, one KV head's
+//    workgroups on one XCD when the KV-head count allows.
+//
+// Layouts: q, dout, out [B, Hq, N, d]; k, v [B, Hkv, N, d]; lse, delta
+// [B, Hq, N]; dq [B, Hq, N, d]; dk, dv [B, Hkv, N, d].  MFMA operand
+// layouts are the ones listed in gqa_device.hpp; LDS tiles are those of
+// prefill_tiles.hpp.
+
+#include "gqa_device.hpp"
+#include "gqa_launch.hpp"
+#include "prefill_tiles.hpp"
+
+namespace gqa {
+
+namespace {
+
+constexpr int kThreads = tiles::kThreads;
+constexpr int kTile = tiles::kRows;   // rows per LDS tile (keys, or query positions)
+constexpr int kDqRows = 128;          // query rows per dQ workgroup
+constexpr int kKeys = 128;            // keys per dK/dV workgroup (32 per wavefront)
+constexpr int kXcds = 8;
+
+// Workgroup -> (unit, tile) with the tile holding the most work first and,
+// when units divide evenly, all tiles of a unit on one XCD (workgroup w runs
+// on XCD w % 8).
+__device__ __forceinline__ void unit_and_tile(int wg, int units, int& unit, int& slot_tile) {
+  if (units % kXcds == 0) {
+    const int xcd = wg % kXcds, slot = wg / kXcds, per = units / kXcds;
+    unit = xcd * per + slot % per;
+    slot_tile = slot / per;
+  } else {
+    unit = wg % units;
+    slot_tile = wg / units;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                    const __bf16* __restrict__ v, const float* __restrict__ out,
+                    const float* __restrict__ lse, const __bf16* __restrict__ dout,
+                    float* __restrict__ dq, float* __restrict__ delta, int hq, int hkv, int n, int g,
+                    int gw, int n_qtiles, int units, float scale_log2, float scale) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kTile * D;
+  __shared__ __align__(16) __bf16 k0s[TILE];
+  __shared__ __align__(16) __bf16 v0s[TILE];
+  __shared__ __align__(16) __bf16 k1s[TILE];
+  __shared__ __align__(16) __bf16 v1s[TILE];
+
+  int unit, back;
+  unit_and_tile(blockIdx.x, units, unit, back);
+  const int qt = n_qtiles - 1 - back;
+  const int nhb = g / gw;
+  const int b = unit / (hkv * nhb);
+  const int rem = unit - b * hkv * nhb;
+  const int kvh = rem / nhb;
+  const int hb = rem - kvh * nhb;
+  const int mq = kDqRows / gw;
+  const int q0 = qt * mq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int row = lane & 31;   // query row within the wave (B/D column)
+  const int j = lane >> 5;     // contraction group
+  const int head = kvh * g + hb * gw + (32 * w) / mq;
+  const int pos0 = q0 + (32 * w) % mq;
+  const int pos = pos0 + row;
+  const size_t row_idx = ((size_t)b * hq + head) * n + min(pos, n - 1);
+
+  // Q^T and dO^T as B operands (8 consecutive columns per contraction
+  // group), and this row's D from the same dO values and out.
+  bf16x8 qb[KSTEPS], ob[KSTEPS];
+  float dpart = 0.f;
+  {
+    const __bf16* qrow = q + row_idx * D;
+    const __bf16* orow = dout + row_idx * D;
+    const float* frow = out + row_idx * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qb[kk] = load_bf16x8(qrow + 16 * kk + 8 * j);
+      ob[kk] = load_bf16x8(orow + 16 * kk + 8 * j);
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(frow + 16 * kk + 8 * j);
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(frow + 16 * kk + 8 * j + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart = __builtin_fmaf((float)ob[kk][e], f0[e], dpart);
+        dpart = __builtin_fmaf((float)ob[kk][4 + e], f1[e], dpart);
+      }
+    }
+  }
+  const float drow = dpart + shfl_xor(dpart, 32);
+  const float lse2 = lse[row_idx] * kLog2e;
+  if (j == 0 && pos < n) delta[row_idx] = drow;
+
+  int a_rd[2][KSTEPS];           // K / V rows: key 32 kb + row, chunk 2 kk + j
+  int t_rd[4][DB], t_dx[4][DB];  // K^T: keys of 16-key chunk c, columns of block db
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) a_rd[kb][kk] = tiles::row_offset<D>(32 * kb + row, 2 * kk + j);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, t_rd[c][db], t_dx[c][db]);
+
+  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, n * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, n * D * 2);
+  const tiles::TileFill<D> fill(tid);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  const int lim = min(pos, n - 1);           // last key this row sees
+  const int wave_hi = min(n, pos0 + 32);     // keys this wavefront needs
+  const int ntiles = (min(n, q0 + mq) + kTile - 1) / kTile;
+
+  auto tile = [&](const __bf16* ks, const __bf16* vs, int t0) {
+    // S^T and dP^T [64 keys, 32 rows] = K Q^T and V dO^T
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(load_bf16x8(ks + a_rd[kb][kk]), qb[kk], sc[kb]);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(load_bf16x8(vs + a_rd[kb][kk]), ob[kk], dp[kb]);
+    // dS^T in the B-operand order of the 16-key chunks: element r of block
+    // kb is key t0 + 32 kb + 8 (r/4) + 4 j + r%4.
+    const bool edge = t0 + kTile > pos0 || t0 + kTile > n;
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -lse2));
+        if (edge) {
+          const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
+          p = t <= lim ? p : 0.f;
+        }
+        dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - drow));
+      }
+    // dQ^T [d, rows] += K^T [d, 16 keys] dS^T [16 keys, rows]
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma32(tiles::read_tr<D>(ks, t_rd[c][db], t_dx[c][db]), dsb[c], acc[db]);
+  };
+
+  fill.issue2(k0s, rk, v0s, rv, w, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) fill.issue2(k1s, rk, v1s, rv, w, (it + 1) * kTile);
+    if (it * kTile < wave_hi) tile(k0s, v0s, it * kTile);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) fill.issue2(k0s, rk, v0s, rv, w, (it + 2) * kTile);
+    if ((it + 1) * kTile < wave_hi) tile(k1s, v1s, (it + 1) * kTile);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (pos < n) {
+    float* drow_out = dq + row_idx * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = acc[db][4 * r4 + r] * scale;
+        *reinterpret_cast<f32x4*>(drow_out + 32 * db + 8 * r4 + 4 * j) = o4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (summed over the group's query heads)
+// ---------------------------------------------------------------------------
+
+// Start the loads of query rows row0 .. row0+63 of one head: its q and dout
+// rows into LDS tiles, and (waves 0 and 1 only) 64 floats of `scalars`
+// (lse or D) into rs[64 w ..].  A plain function rather than a lambda: the
+// host pass cannot form buffer resources, and a kernel whose lambda builds
+// one silently loses its host launch stub.
+template <int D>
+__device__ __forceinline__ void issue_rows(const tiles::TileFill<D>& fill, const __bf16* qh,
+                                           const __bf16* oh, const float* scalars, __bf16* qs, __bf16* os,
+                                           float* rs, int n, int w, int row0, int lane) {
+  fill.issue2(qs, make_rsrc(qh, n * D * 2), os, make_rsrc(oh, n * D * 2), w, row0);
+  if (w < 2) tiles::load_floats_lds(rs + w * kTile, make_rsrc(scalars, n * 4), (row0 + lane) * 4);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                      const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                      const float* __restrict__ lse, const float* __restrict__ delta,
+                      float* __restrict__ dk, float* __restrict__ dv, int hq, int hkv, int n, int g,
+                      int units, float scale_log2, float scale) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kTile * D;
+  __shared__ __align__(16) __bf16 q0s[TILE];
+  __shared__ __align__(16) __bf16 o0s[TILE];
+  __shared__ __align__(16) __bf16 q1s[TILE];
+  __shared__ __align__(16) __bf16 o1s[TILE];
+  __shared__ __align__(16) float r0s[2 * kTile];   // lse, then D, of the stage's rows
+  __shared__ __align__(16) float r1s[2 * kTile];
+
+  int unit, kt;
+  unit_and_tile(blockIdx.x, units, unit, kt);
+  const int b = unit / hkv;
+  const int kvh = unit - b * hkv;
+  const int k0 = kt * kKeys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int col = lane & 31;   // this lane's key within the wave (A row / D row index)
+  const int j = lane >> 5;     // contraction group
+  const int kw = k0 + 32 * w;  // the wave's first key
+
+  // K and V rows of key kw + col as B operands of S = Q K^T and dP = dO V^T.
+  const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
+  bf16x8 kb[KSTEPS], vb[KSTEPS];
+  {
+    const int key = kw + col;
+    const __bf16* krow = k + kv_off + (size_t)min(key, n - 1) * D;
+    const __bf16* vrow = v + kv_off + (size_t)min(key, n - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      kb[kk] = load_bf16x8(krow + 16 * kk + 8 * j);
+      vb[kk] = load_bf16x8(vrow + 16 * kk + 8 * j);
+      if (key >= n) kb[kk] = vb[kk] = bf16x8{};
+    }
+  }
+
+  int a_rd[2][KSTEPS];           // Q / dO rows 32 rb + col, chunk 2 kk + j
+  int t_rd[4][DB], t_dx[4][DB];  // Q^T / dO^T: rows of 16-row chunk c, columns of block db
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) a_rd[rb][kk] = tiles::row_offset<D>(32 * rb + col, 2 * kk + j);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, t_rd[c][db], t_dx[c][db]);
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dka[i] = dva[i] = f32x16{};
+
+  // Steps: q-tiles from the last down to the one holding key k0, each for
+  // the g query heads of the group.
+  const int qt_last = (n - 1) / kTile;
+  const int qt_first = k0 / kTile;
+  const int nsteps = (qt_last - qt_first + 1) * g;
+  const tiles::TileFill<D> fill(tid);
+
+  // Loads of step s into one stage: the Q and dO tiles, and one float per
+  // lane from waves 0 (lse) and 1 (D), zeros past n.
+  auto issue = [&](int s, __bf16* qs, __bf16* os, float* rs) {
+    const int qt = qt_last - s / g;
+    const size_t hrow = ((size_t)b * hq + kvh * g + s % g) * n;
+    issue_rows<D>(fill, q + hrow * D, dout + hrow * D, (w == 0 ? lse : delta) + hrow, qs, os, rs, n, w,
+                  qt * kTile, lane);
+  };
+
+  auto step = [&](int s, const __bf16* qs, const __bf16* os, const float* rs) {
+    const int i0 = (qt_last - s / g) * kTile;
+    if (i0 + kTile - 1 < kw) return;   // every row of the tile precedes the wave's keys
+    const bool edge = i0 < kw + 32 || i0 + kTile > n;
+    const int key = kw + col;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // S and dP [32 rows, 32 keys]: element r is row i0 + 32 rb + 8 (r/4) + 4 j + r%4.
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) sc = mfma32(load_bf16x8(qs + a_rd[rb][kk]), kb[kk], sc);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) dp = mfma32(load_bf16x8(os + a_rd[rb][kk]), vb[kk], dp);
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        l4[r4] = *reinterpret_cast<const f32x4*>(rs + 32 * rb + 8 * r4 + 4 * j);
+        d4[r4] = *reinterpret_cast<const f32x4*>(rs + kTile + 32 * rb + 8 * r4 + 4 * j);
+      }
+      // P^T and dS^T as A operands: lane = key, k-group j = the rows above.
+      bf16x8 pa[2], da[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l4[r >> 2][r & 3] * kLog2e));
+        if (edge) {
+          const int i = i0 + 32 * rb + 8 * (r >> 2) + 4 * j + (r & 3);
+          p = (key <= i && i < n) ? p : 0.f;
+        }
+        pa[r >> 3][r & 7] = (__bf16)p;
+        da[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[r >> 2][r & 3]));
+      }
+      // dV += P^T dO and dK += dS^T Q over the block's two 16-row chunks.
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int c = 2 * rb + c2;
+          dva[db] = mfma32(pa[c2], tiles::read_tr<D>(os, t_rd[c][db], t_dx[c][db]), dva[db]);
+          dka[db] = mfma32(da[c2], tiles::read_tr<D>(qs, t_rd[c][db], t_dx[c][db]), dka[db]);
+        }
+    }
+  };
+
+  issue(0, q0s, o0s, r0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
+    step(s, q0s, o0s, r0s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    if (s + 2 < nsteps) issue(s + 2, q0s, o0s, r0s);
+    step(s + 1, q1s, o1s, r1s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // D rows of dK/dV: key kw + 8 (r/4) + 4 j + r%4, column 32 db + col.
+  float* dk_b = dk + kv_off;
+  float* dv_b = dv + kv_off;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kw + 8 * (r >> 2) + 4 * j + (r & 3);
+    if (key < n) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dk_b[(size_t)key * D + 32 * db + col] = dka[db][r] * scale;
+        dv_b[(size_t)key * D + 32 * db + col] = dva[db][r];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* out,
+                                   const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                   float* delta, const PrefillShape& s, hipStream_t stream) {
+  const int g = s.hq / s.hkv;
+  const int gw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int mq = kDqRows / gw;
+  const int n_qtiles = (s.n + mq - 1) / mq;
+  const int dq_units = s.batch * s.hkv * (g / gw);
+  const int kv_units = s.batch * s.hkv;
+  const int n_ktiles = (s.n + kKeys - 1) / kKeys;
+  const float sl2 = s.scale * kLog2e;
+  auto qp = static_cast<const __bf16*>(q);
+  auto kp = static_cast<const __bf16*>(k);
+  auto vp = static_cast<const __bf16*>(v);
+  auto op = static_cast<const __bf16*>(dout);
+  const dim3 block(kThreads);
+  const dim3 grid_dq((unsigned)dq_units * (unsigned)n_qtiles);
+  const dim3 grid_kv((unsigned)kv_units * (unsigned)n_ktiles);
+  if (s.d == 128) {
+    hipLaunchKernelGGL(prefill_bwd_dq<128>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, delta,
+                       s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
+    hipLaunchKernelGGL(prefill_bwd_dkdv<128>, grid_kv, block, 0, stream, qp, kp, vp, op, lse, delta, dk,
+                       dv, s.hq, s.hkv, s.n, g, kv_units, sl2, s.scale);
+  } else {
+    hipLaunchKernelGGL(prefill_bwd_dq<64>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, delta,
+                       s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
+    hipLaunchKernelGGL(prefill_bwd_dkdv<64>, grid_kv, block, 0, stream, qp, kp, vp, op, lse, delta, dk,
+                       dv, s.hq, s.hkv, s.n, g, kv_units, sl2, s.scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

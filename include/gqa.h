@@ -52,7 +52,7 @@ typedef enum gqa_status {
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
   GQA_ERR_SHAPE = 2,       /* size < 1, Hkv not dividing Hq, or size overflow    */
   GQA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype not allowed, bad range  */
-  GQA_ERR_WORKSPACE = 4,   /* workspace smaller than gqa_decode_plan requires    */
+  GQA_ERR_WORKSPACE = 4,   /* workspace smaller than the planning call requires  */
   GQA_ERR_HIP = 5,         /* the HIP runtime rejected a launch                  */
   GQA_ERR_ALIGN = 6        /* a pointer violates the alignment rule above        */
 } gqa_status;
@@ -241,11 +241,58 @@ int32_t gqa_decode_fp8_split(const void* q, const void* k_cache, const void* v_c
  *   lse  [batch, num_q_heads, seq_len] float32 natural log-sum-exp of the
  *        scaled scores of each row, or NULL to skip it
  *   dtype must be GQA_BF16; head_dim 64 or 128.
+ * Limits: seq_len * head_dim * 4 < 2^31 (GQA_ERR_SHAPE otherwise).
  */
 int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* out,
                            float* lse, int32_t batch, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t seq_len, int32_t head_dim,
                            float scale, int32_t dtype, void* stream);
+
+/*
+ * Workspace bytes that gqa_prefill_causal_backward needs for this shape
+ * (one float per query row, rounded up to 256 bytes).  Same shape rules and
+ * statuses as gqa_prefill_causal with dtype GQA_BF16.
+ */
+int32_t gqa_prefill_backward_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t seq_len, int32_t head_dim,
+                                       int64_t* workspace_bytes_out);
+
+/*
+ * Gradients of causal GQA prefill (the training backward pass).  A shared
+ * K or V row collects gradient from every query head of its group: dk and
+ * dv of KV head j are sums over query heads j*g .. j*g+g-1, formed inside
+ * the library without copying K/V per query head and without per-head
+ * gradient buffers (study.greatitself.com, "Grouped-Query and Multi-Query
+ * Attention", section "Share keys and values without confusing query-head
+ * identity", training paragraph).  With P the causal softmax of one query
+ * head and dout the gradient of the loss with respect to its output:
+ *
+ *     dv[j] = sum_h P_h^T dout_h            dS_h = P_h * (dout_h V^T - rowsum(dout_h * out_h))
+ *     dq_h  = scale dS_h K[j]               dk[j] = scale sum_h dS_h^T q_h
+ *
+ *   q, dout [batch, num_q_heads, seq_len, head_dim]   bf16
+ *   k, v    [batch, num_kv_heads, seq_len, head_dim]  bf16
+ *   out     [batch, num_q_heads, seq_len, head_dim]   float32, and
+ *   lse     [batch, num_q_heads, seq_len]             float32: the out and lse
+ *           that gqa_prefill_causal returned for the same q, k, v and scale
+ *           (P is recomputed from lse; out only enters rowsum(dout * out))
+ *   dq      [batch, num_q_heads, seq_len, head_dim]   float32, overwritten
+ *   dk, dv  [batch, num_kv_heads, seq_len, head_dim]  float32, overwritten
+ *   workspace   device scratch of at least gqa_prefill_backward_workspace
+ *               bytes, 16-byte aligned; its contents on entry do not matter
+ *   dtype must be GQA_BF16; head_dim 64 or 128.
+ *
+ * Two kernels run in order on `stream`; results are bitwise reproducible
+ * (no atomics).  Errors: GQA_ERR_NULL for any NULL pointer (lse is required
+ * here), GQA_ERR_WORKSPACE for a short workspace, otherwise as
+ * gqa_prefill_causal.
+ */
+int32_t gqa_prefill_causal_backward(const void* q, const void* k, const void* v, const float* out,
+                                    const float* lse, const void* dout, float* dq, float* dk,
+                                    float* dv, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t seq_len, int32_t head_dim,
+                                    float scale, int32_t dtype, void* workspace,
+                                    int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -118,6 +118,33 @@ def test_prefill_validation(lib):
     assert call(lse=ctypes.c_void_p(0x100002)) == ALIGN
 
 
+def test_prefill_backward_validation(lib):
+    ws_need = ctypes.c_int64()
+    assert lib.gqa_prefill_backward_workspace(2, 8, 2, 100, 128, ctypes.byref(ws_need)) == OK
+    assert ws_need.value == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert lib.gqa_prefill_backward_workspace(2, 8, 3, 100, 128, ctypes.byref(ws_need)) == SHAPE
+    assert lib.gqa_prefill_backward_workspace(2, 8, 2, 100, 128, None) == NULL
+
+    def call(q=FAKE, lse=FAKE, dout=FAKE, dk=FAKE, ws=FAKE, ws_bytes=1 << 20, B=1, hq=8, hkv=2, n=128,
+             d=128, dtype=BF16):
+        return lib.gqa_prefill_causal_backward(q, FAKE, FAKE, FAKE, lse, dout, FAKE, dk, FAKE, B, hq, hkv,
+                                               n, d, 0.1, dtype, ws, ws_bytes, None)
+    assert call(q=None) == NULL
+    assert call(lse=None) == NULL
+    assert call(dout=None) == NULL
+    assert call(dk=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(hkv=3) == SHAPE
+    assert call(n=0) == SHAPE
+    assert call(n=1 << 23) == SHAPE      # one head's rows would pass 2 GiB of buffer offsets
+    assert call(d=96) == UNSUP
+    assert call(dtype=F32) == UNSUP
+    assert call(ws_bytes=8 * 128 * 4 - 1) == WS
+    assert call(dout=MISALIGNED) == ALIGN
+    assert call(ws=MISALIGNED) == ALIGN
+    assert call(lse=ctypes.c_void_p(0x100002)) == ALIGN
+
+
 def test_python_binding_raises_without_gpu_work():
     import torch
     q = torch.zeros(1, 8, 64)
