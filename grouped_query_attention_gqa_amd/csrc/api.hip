@@ -92,9 +92,10 @@ int32_t check_prefill(int32_t batch, int32_t hq, int32_t hkv, int32_t n, int32_t
   return GQA_OK;
 }
 
-// The backward's workspace is D = rowsum(dout * out), one float per query row.
+// The backward's workspace holds two floats per query row: lse * log2(e)
+// and D = rowsum(dout * out).
 int64_t backward_workspace_bytes(int32_t batch, int32_t hq, int32_t n) {
-  return ((int64_t)batch * hq * n * 4 + 255) / 256 * 256;
+  return ((int64_t)batch * hq * n * 8 + 255) / 256 * 256;
 }
 
 }  // namespace

@@ -66,10 +66,10 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, fl
                                  float* lse, const PrefillShape& s, hipStream_t stream);
 
 // Backward of causal prefill: dq, then (after it, on the same stream) dk and
-// dv; `delta` [batch, hq, n] receives rowsum(dout * out) from the first
-// kernel and is read by the second.
+// dv; `row_terms` [2][batch, hq, n] receives lse * log2(e) and
+// rowsum(dout * out) from the first kernel and is read by the second.
 hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* out,
                                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                                   float* delta, const PrefillShape& s, hipStream_t stream);
+                                   float* row_terms, const PrefillShape& s, hipStream_t stream);
 
 }  // namespace gqa

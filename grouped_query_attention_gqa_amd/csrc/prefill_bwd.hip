@@ -19,7 +19,7 @@
 //    (the forward's partition: Gw heads x 128/Gw positions), streams the K/V
 //    tiles of keys up to its diagonal through LDS and accumulates dQ^T in
 //    registers.  Its prologue forms D for its rows from out and dO and
-//    stores it for the second kernel.
+//    stores it, with lse in the log2 domain, for the second kernel.
 //  * prefill_bwd_dkdv: a workgroup owns 128 keys of one KV head (32 per
 //    wavefront, with K and V held in registers as MFMA operands) and
 //    streams, through double-buffered LDS, the Q/dO tiles of every query
@@ -31,8 +31,9 @@
 //    workgroups are issued heaviest (first keys) first, one KV head's
 //    workgroups on one XCD when the KV-head count allows.
 //
-// Layouts: q, dout, out [B, Hq, N, d]; k, v [B, Hkv, N, d]; lse, delta
-// [B, Hq, N]; dq [B, Hq, N, d]; dk, dv [B, Hkv, N, d].  MFMA operand
+// Layouts: q, dout, out [B, Hq, N, d]; k, v [B, Hkv, N, d]; lse [B, Hq, N];
+// row_terms [2][B, Hq, N] (lse * log2 e, then D); dq [B, Hq, N, d]; dk, dv
+// [B, Hkv, N, d].  MFMA operand
 // layouts are the ones listed in gqa_device.hpp; LDS tiles are those of
 // prefill_tiles.hpp.
 
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const float* __restrict__ out,
                     const float* __restrict__ lse, const __bf16* __restrict__ dout,
-                    float* __restrict__ dq, float* __restrict__ delta, int hq, int hkv, int n, int g,
-                    int gw, int n_qtiles, int units, float scale_log2, float scale) {
+                    float* __restrict__ dq, float* __restrict__ row_terms, size_t rows, int hq, int hkv,
+                    int n, int g, int gw, int n_qtiles, int units, float scale_log2, float scale) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kTile * D;
@@ -127,7 +128,8 @@ void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
   const float drow = dpart + shfl_xor(dpart, 32);
   const float lse2 = lse[row_idx] * kLog2e;
-  if (j == 0 && pos < n) delta[row_idx] = drow;
+  // row_terms[0] = lse * log2(e), row_terms[1] = D, each [B, Hq, N]
+  if (pos < n) row_terms[(size_t)j * rows + row_idx] = j == 0 ? lse2 : drow;
 
   int a_rd[2][KSTEPS];           // K / V rows: key 32 kb + row, chunk 2 kk + j
   int t_rd[4][DB], t_dx[4][DB];  // K^T: keys of 16-key chunk c, columns of block db
@@ -234,13 +236,157 @@ __device__ __forceinline__ void issue_rows(const tiles::TileFill<D>& fill, const
   if (w < 2) tiles::load_floats_lds(rs + w * kTile, make_rsrc(scalars, n * 4), (row0 + lane) * 4);
 }
 
+// P^T and dS^T of one 32-row block as bf16 A operands (lane = key, k-group
+// j = rows 16 c + 4 j + 0..3 and 16 c + 8 + 4 j + 0..3 for chunk c), from
+// S and dP (element r: row 8 (r/4) + 4 j + r%4 of the block).  With MASK,
+// `rel` is the lane's key minus the block's first row: rows before the key
+// get P = 0.
+template <bool MASK>
+__device__ __forceinline__ void softmax_grad_block(const f32x16& sc, const f32x16& dp, const float* rs_lse,
+                                                   const float* rs_d, float scale_log2, int j, int rel,
+                                                   bf16x8 (&pa)[2], bf16x8 (&da)[2]) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(rs_lse + 8 * r4 + 4 * j);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(rs_d + 8 * r4 + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * r4 + e;
+      float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l4[e]));
+      if (MASK) p = (8 * r4 + 4 * j + e >= rel) ? p : 0.f;
+      pa[r >> 3][r & 7] = (__bf16)p;
+      da[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]));
+    }
+  }
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x2;
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+
+// Transposed LDS operands of 16-row chunk c: dO^T and Q^T for all column blocks.
+template <int D>
+__device__ __forceinline__ void read_chunk_tr(const __bf16* qs, const __bf16* os, const int (&t_rd)[4][D / 32],
+                                              const int (&t_dx)[4][D / 32], int c, bf16x8 (&ot)[D / 32],
+                                              bf16x8 (&qt)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    ot[db] = tiles::read_tr<D>(os, t_rd[c][db], t_dx[c][db]);
+    qt[db] = tiles::read_tr<D>(qs, t_rd[c][db], t_dx[c][db]);
+  }
+}
+
+// One 64-row Q/dO tile against the wavefront's 32 keys: S and dP for the
+// two 32-row blocks, then dV += P^T dO and dK += dS^T Q chunk by chunk.
+// With one wavefront per SIMD nothing else hides LDS latency, so the code is
+// software-pipelined by hand: the LDS operands of each group of MFMAs are
+// read while the previous group runs, and the softmax arithmetic of a block
+// is interleaved with MFMAs that do not depend on it.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_step(const __bf16* qs, const __bf16* os, const float* rs,
+                                          const bf16x8 (&kb)[D / 16], const bf16x8 (&vb)[D / 16],
+                                          const int (&a_rd)[2][D / 16], const int (&t_rd)[4][D / 32],
+                                          const int (&t_dx)[4][D / 32], f32x16 (&dka)[D / 32],
+                                          f32x16 (&dva)[D / 32], float scale_log2, int j, int rel) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  f32x16 sc0 = f32x16{}, dp0 = f32x16{}, sc1 = f32x16{}, dp1 = f32x16{};
+  bf16x8 qa[KSTEPS], oa[KSTEPS], qa1[KSTEPS], oa1[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    qa[kk] = load_bf16x8(qs + a_rd[0][kk]);
+    oa[kk] = load_bf16x8(os + a_rd[0][kk]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // S, dP of rows 0..31; the row operands of rows 32..63 load meanwhile.
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    sc0 = mfma32(qa[kk], kb[kk], sc0);
+    dp0 = mfma32(oa[kk], vb[kk], dp0);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    qa1[kk] = load_bf16x8(qs + a_rd[1][kk]);
+    oa1[kk] = load_bf16x8(os + a_rd[1][kk]);
+  }
+#pragma unroll
+  for (int i = 0; i < KSTEPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // S, dP of rows 32..63; the transposed operands of chunk 0 load meanwhile.
+  bf16x8 ot[2][DB], qt[2][DB];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    sc1 = mfma32(qa1[kk], kb[kk], sc1);
+    dp1 = mfma32(oa1[kk], vb[kk], dp1);
+  }
+  read_chunk_tr<D>(qs, os, t_rd, t_dx, 0, ot[0], qt[0]);
+#pragma unroll
+  for (int i = 0; i < 2 * KSTEPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 pa0[2], da0[2], pa1[2], da1[2];
+  softmax_grad_block<MASK>(sc0, dp0, rs, rs + kTile, scale_log2, j, rel, pa0, da0);
+  __builtin_amdgcn_sched_barrier(0);
+  // Chunks 0 and 1 (rows 0..31) while the operands of the next chunk load;
+  // the softmax of rows 32..63 is spread over chunk 1's MFMAs.
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dva[db] = mfma32(pa0[0], ot[0][db], dva[db]);
+    dka[db] = mfma32(da0[0], qt[0][db], dka[db]);
+  }
+  read_chunk_tr<D>(qs, os, t_rd, t_dx, 1, ot[1], qt[1]);
+#pragma unroll
+  for (int i = 0; i < 2 * DB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dva[db] = mfma32(pa0[1], ot[1][db], dva[db]);
+    dka[db] = mfma32(da0[1], qt[1][db], dka[db]);
+  }
+  read_chunk_tr<D>(qs, os, t_rd, t_dx, 2, ot[0], qt[0]);
+  softmax_grad_block<MASK>(sc1, dp1, rs + 32, rs + kTile + 32, scale_log2, j, rel - 32, pa1, da1);
+#pragma unroll
+  for (int i = 0; i < 2 * DB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 3);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 3);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dva[db] = mfma32(pa1[0], ot[0][db], dva[db]);
+    dka[db] = mfma32(da1[0], qt[0][db], dka[db]);
+  }
+  read_chunk_tr<D>(qs, os, t_rd, t_dx, 3, ot[1], qt[1]);
+#pragma unroll
+  for (int i = 0; i < 2 * DB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dva[db] = mfma32(pa1[1], ot[1][db], dva[db]);
+    dka[db] = mfma32(da1[1], qt[1][db], dka[db]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                       const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-                      const float* __restrict__ lse, const float* __restrict__ delta,
-                      float* __restrict__ dk, float* __restrict__ dv, int hq, int hkv, int n, int g,
-                      int units, float scale_log2, float scale) {
+                      const float* __restrict__ row_terms, size_t rows, float* __restrict__ dk,
+                      float* __restrict__ dv, int hq, int hkv, int n, int g, int units, float scale_log2,
+                      float scale) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kTile * D;
@@ -259,7 +405,7 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // this lane's key within the wave (A row / D row index)
   const int j = lane >> 5;     // contraction group
   const int kw = k0 + 32 * w;  // the wave's first key
@@ -281,14 +427,29 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 
   int a_rd[2][KSTEPS];           // Q / dO rows 32 rb + col, chunk 2 kk + j
   int t_rd[4][DB], t_dx[4][DB];  // Q^T / dO^T: rows of 16-row chunk c, columns of block db
+  // The swizzle depends on the row modulo 16, so the offsets of row blocks
+  // 32 rb and chunks 16 c are those of block 0 plus a constant.  The empty
+  // asm hides the base offsets' value range from the compiler, which then
+  // adds stage and block constants through the LDS instructions' offset
+  // field instead of spending a VALU op per read on an OR.
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    int base = tiles::row_offset<D>(col, 2 * kk + j);
+    asm volatile("" : "+v"(base));
+    a_rd[0][kk] = base;
+    a_rd[1][kk] = base + 32 * D;
+  }
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) a_rd[rb][kk] = tiles::row_offset<D>(32 * rb + col, 2 * kk + j);
+  for (int db = 0; db < DB; ++db) {
+    int base, dx;
+    tiles::tr_offsets<D>(lane, 0, db, base, dx);
+    asm volatile("" : "+v"(base));
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, t_rd[c][db], t_dx[c][db]);
+    for (int c = 0; c < 4; ++c) {
+      t_rd[c][db] = base + 16 * D * c;
+      t_dx[c][db] = dx;
+    }
+  }
 
   f32x16 dka[DB], dva[DB];
 #pragma unroll
@@ -306,66 +467,56 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
   auto issue = [&](int s, __bf16* qs, __bf16* os, float* rs) {
     const int qt = qt_last - s / g;
     const size_t hrow = ((size_t)b * hq + kvh * g + s % g) * n;
-    issue_rows<D>(fill, q + hrow * D, dout + hrow * D, (w == 0 ? lse : delta) + hrow, qs, os, rs, n, w,
+    issue_rows<D>(fill, q + hrow * D, dout + hrow * D, row_terms + (w == 1 ? rows : 0) + hrow, qs, os, rs, n, w,
                   qt * kTile, lane);
   };
 
-  auto step = [&](int s, const __bf16* qs, const __bf16* os, const float* rs) {
+  // Only the last two q-tiles (the last 2 g steps) reach below a key of the
+  // workgroup and need the causal mask; every earlier step runs the
+  // mask-free body, in a loop of its own so that the accumulators never
+  // cross a branch.  Rows past n need no mask either: their q, dout, lse and
+  // D arrive as zeros, so their P = 1 meets zero dout and zero dS.
+  const int n_plain = nsteps - min(nsteps, 2 * g);
+  auto plain = [&](const __bf16* qs, const __bf16* os, const float* rs) {
+    dkdv_step<D, false>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, 0);
+  };
+  auto masked = [&](int s, const __bf16* qs, const __bf16* os, const float* rs) {
     const int i0 = (qt_last - s / g) * kTile;
     if (i0 + kTile - 1 < kw) return;   // every row of the tile precedes the wave's keys
-    const bool edge = i0 < kw + 32 || i0 + kTile > n;
-    const int key = kw + col;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // S and dP [32 rows, 32 keys]: element r is row i0 + 32 rb + 8 (r/4) + 4 j + r%4.
-      f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) sc = mfma32(load_bf16x8(qs + a_rd[rb][kk]), kb[kk], sc);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) dp = mfma32(load_bf16x8(os + a_rd[rb][kk]), vb[kk], dp);
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        l4[r4] = *reinterpret_cast<const f32x4*>(rs + 32 * rb + 8 * r4 + 4 * j);
-        d4[r4] = *reinterpret_cast<const f32x4*>(rs + kTile + 32 * rb + 8 * r4 + 4 * j);
-      }
-      // P^T and dS^T as A operands: lane = key, k-group j = the rows above.
-      bf16x8 pa[2], da[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l4[r >> 2][r & 3] * kLog2e));
-        if (edge) {
-          const int i = i0 + 32 * rb + 8 * (r >> 2) + 4 * j + (r & 3);
-          p = (key <= i && i < n) ? p : 0.f;
-        }
-        pa[r >> 3][r & 7] = (__bf16)p;
-        da[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[r >> 2][r & 3]));
-      }
-      // dV += P^T dO and dK += dS^T Q over the block's two 16-row chunks.
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int c = 2 * rb + c2;
-          dva[db] = mfma32(pa[c2], tiles::read_tr<D>(os, t_rd[c][db], t_dx[c][db]), dva[db]);
-          dka[db] = mfma32(da[c2], tiles::read_tr<D>(qs, t_rd[c][db], t_dx[c][db]), dka[db]);
-        }
-    }
+    dkdv_step<D, true>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, kw + col - i0);
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next step have landed
+    __syncthreads();                 // ... everyone's, and everyone is done with the current stage
   };
 
+  // Stage 0 holds even steps, stage 1 odd ones.
   issue(0, q0s, o0s, r0s);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
-    step(s, q0s, o0s, r0s);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (s + 1 >= nsteps) break;
+  sync();
+  int s = 0;
+  for (; s + 1 < n_plain; s += 2) {
+    issue(s + 1, q1s, o1s, r1s);
+    plain(q0s, o0s, r0s);
+    sync();
     if (s + 2 < nsteps) issue(s + 2, q0s, o0s, r0s);
-    step(s + 1, q1s, o1s, r1s);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    plain(q1s, o1s, r1s);
+    sync();
+  }
+  if (s < n_plain) {
+    if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
+    plain(q0s, o0s, r0s);
+    sync();
+    ++s;
+  }
+  for (; s < nsteps; ++s) {
+    if (s & 1) {
+      if (s + 1 < nsteps) issue(s + 1, q0s, o0s, r0s);
+      masked(s, q1s, o1s, r1s);
+    } else {
+      if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
+      masked(s, q0s, o0s, r0s);
+    }
+    sync();
   }
 
   // D rows of dK/dV: key kw + 8 (r/4) + 4 j + r%4, column 32 db + col.
@@ -388,7 +539,7 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 
 hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* out,
                                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                                   float* delta, const PrefillShape& s, hipStream_t stream) {
+                                   float* row_terms, const PrefillShape& s, hipStream_t stream) {
   const int g = s.hq / s.hkv;
   const int gw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
   const int mq = kDqRows / gw;
@@ -396,6 +547,7 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   const int dq_units = s.batch * s.hkv * (g / gw);
   const int kv_units = s.batch * s.hkv;
   const int n_ktiles = (s.n + kKeys - 1) / kKeys;
+  const size_t rows = (size_t)s.batch * s.hq * s.n;
   const float sl2 = s.scale * kLog2e;
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<const __bf16*>(k);
@@ -405,14 +557,14 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   const dim3 grid_dq((unsigned)dq_units * (unsigned)n_qtiles);
   const dim3 grid_kv((unsigned)kv_units * (unsigned)n_ktiles);
   if (s.d == 128) {
-    hipLaunchKernelGGL(prefill_bwd_dq<128>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, delta,
-                       s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
-    hipLaunchKernelGGL(prefill_bwd_dkdv<128>, grid_kv, block, 0, stream, qp, kp, vp, op, lse, delta, dk,
+    hipLaunchKernelGGL(prefill_bwd_dq<128>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, row_terms,
+                       rows, s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
+    hipLaunchKernelGGL(prefill_bwd_dkdv<128>, grid_kv, block, 0, stream, qp, kp, vp, op, row_terms, rows, dk,
                        dv, s.hq, s.hkv, s.n, g, kv_units, sl2, s.scale);
   } else {
-    hipLaunchKernelGGL(prefill_bwd_dq<64>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, delta,
-                       s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
-    hipLaunchKernelGGL(prefill_bwd_dkdv<64>, grid_kv, block, 0, stream, qp, kp, vp, op, lse, delta, dk,
+    hipLaunchKernelGGL(prefill_bwd_dq<64>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, row_terms,
+                       rows, s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
+    hipLaunchKernelGGL(prefill_bwd_dkdv<64>, grid_kv, block, 0, stream, qp, kp, vp, op, row_terms, rows, dk,
                        dv, s.hq, s.hkv, s.n, g, kv_units, sl2, s.scale);
   }
   return hipGetLastError();

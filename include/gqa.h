@@ -250,7 +250,7 @@ int32_t gqa_prefill_causal(const void* q, const void* k, const void* v, float* o
 
 /*
  * Workspace bytes that gqa_prefill_causal_backward needs for this shape
- * (one float per query row, rounded up to 256 bytes).  Same shape rules and
+ * (two floats per query row, rounded up to 256 bytes).  Same shape rules and
  * statuses as gqa_prefill_causal with dtype GQA_BF16.
  */
 int32_t gqa_prefill_backward_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -121,7 +121,7 @@ def test_prefill_validation(lib):
 def test_prefill_backward_validation(lib):
     ws_need = ctypes.c_int64()
     assert lib.gqa_prefill_backward_workspace(2, 8, 2, 100, 128, ctypes.byref(ws_need)) == OK
-    assert ws_need.value == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert ws_need.value == (2 * 8 * 100 * 8 + 255) // 256 * 256
     assert lib.gqa_prefill_backward_workspace(2, 8, 3, 100, 128, ctypes.byref(ws_need)) == SHAPE
     assert lib.gqa_prefill_backward_workspace(2, 8, 2, 100, 128, None) == NULL
 
@@ -139,7 +139,7 @@ def test_prefill_backward_validation(lib):
     assert call(n=1 << 23) == SHAPE      # one head's rows would pass 2 GiB of buffer offsets
     assert call(d=96) == UNSUP
     assert call(dtype=F32) == UNSUP
-    assert call(ws_bytes=8 * 128 * 4 - 1) == WS
+    assert call(ws_bytes=8 * 128 * 8 - 1) == WS
     assert call(dout=MISALIGNED) == ALIGN
     assert call(ws=MISALIGNED) == ALIGN
     assert call(lse=ctypes.c_void_p(0x100002)) == ALIGN
