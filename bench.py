@@ -7,7 +7,8 @@ Default workload (one JSON line on stdout):
   decode call (split kernel + log-sum-exp merge) over the whole batch.
   value = KV-cache bytes read per step / step time (GB/s).
   The same run also times causal prefill (B=2, Hq=32, Hkv=8, N=4096, d=128)
-  and reports its TFLOP/s in the "prefill" object.
+  and its backward (dq, dk, dv) and reports their TFLOP/s in the "prefill"
+  and "prefill_backward" objects.
 
 Inputs are seeded synthetic N(0,1) values; K/V are resident in HBM before the
 timed region and rotated over several copies so the 256 MB MALL cannot serve
@@ -43,7 +44,9 @@ CSRC = os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc")
 # while their digest is unchanged)
 KERNEL_SOURCES = {
     "decode_split": ("decode.hip", "api.hip", "gqa_device.hpp", "gqa_launch.hpp"),
-    "prefill_causal": ("prefill.hip", "gqa_device.hpp", "gqa_launch.hpp"),
+    "prefill_causal": ("prefill.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
+    "prefill_bwd_dq": ("prefill_bwd.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
+    "prefill_bwd_dkdv": ("prefill_bwd.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
 }
 
 
@@ -76,6 +79,12 @@ def decode_flops(seq_lens, hq, d):
 def prefill_flops(b, hq, n, d):
     """Exact causal count: row i attends i+1 keys at 4*d FLOPs per key."""
     return 4 * b * hq * d * n * (n + 1) // 2
+
+
+def prefill_backward_flops(b, hq, n, d):
+    """Algorithmic FLOPs of the causal backward: five products of the
+    forward's size (S recomputed, dP, dV, dQ, dK), 2.5x the forward."""
+    return 2.5 * prefill_flops(b, hq, n, d)
 
 
 def prefill_bytes(b, hq, hkv, n, d):
@@ -122,9 +131,11 @@ def load_counters(kernel: str, workload: str):
 
 
 CALIBRATION_BYTES = 256 * 2 ** 20   # read and written by the --calibration-copy kernel
-COUNTED_KERNELS = {   # kernel-name substring -> (entry kernel, sources key)
+COUNTED_KERNELS = {   # kernel-name substring -> sources key
     "decode_split_bf16": "decode_split",
     "prefill_causal_bf16": "prefill_causal",
+    "prefill_bwd_dq": "prefill_bwd_dq",
+    "prefill_bwd_dkdv": "prefill_bwd_dkdv",
 }
 
 
@@ -156,7 +167,7 @@ def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
            "kernels": {}}
     for name in fetch:
-        wl = "prefill-4k" if name == "prefill_causal" else workload
+        wl = "prefill-4k" if name.startswith("prefill") else workload
         fb, wb = fetch[name] * 1024 * ff, write.get(name, 0.0) * 1024 * wf
         out["kernels"][f"{name}|{wl}"] = {
             "source_digest": kernel_source_digest(name),
@@ -393,6 +404,43 @@ def main():
                          "algorithmic_flops": fl,
                          "algorithmic_bytes": prefill_bytes(pc.batch, pc.num_q_heads, pc.num_kv_heads,
                                                             pc.seq_len, pc.head_dim)},
+        }
+
+        # backward of the same prefill: dq, dk, dv from (q, k, v, out, lse, dout)
+        pdo = torch.from_numpy(gi.make_dout(pc).view(np.int16)).view(torch.bfloat16).cuda()
+        plse = torch.empty(pc.batch, pc.num_q_heads, pc.seq_len, dtype=torch.float32, device="cuda")
+        gqa.gqa_prefill_causal(pq, pk, pv, scale=pc.scale, out=pout, lse=plse)
+        grads = (torch.empty_like(pout),
+                 torch.empty(pc.batch, pc.num_kv_heads, pc.seq_len, pc.head_dim, dtype=torch.float32,
+                             device="cuda"),
+                 torch.empty(pc.batch, pc.num_kv_heads, pc.seq_len, pc.head_dim, dtype=torch.float32,
+                             device="cuda"))
+        bws = torch.empty(gqa.gqa_prefill_backward_workspace(pc.batch, pc.num_q_heads, pc.num_kv_heads,
+                                                             pc.seq_len, pc.head_dim),
+                          dtype=torch.uint8, device="cuda")
+
+        def bstep(i):
+            gqa.gqa_prefill_causal_backward(pq, pk, pv, pout, plse, pdo, scale=pc.scale, workspace=bws,
+                                            grads=grads)
+
+        for i in range(max(3, args.warmup // 2)):
+            bstep(i)
+        bms = event_time_ms(bstep, max(10, args.steps // 2), torch)
+        bfl = prefill_backward_flops(pc.batch, pc.num_q_heads, pc.seq_len, pc.head_dim)
+        btf = bfl / (bms * 1e-3) / 1e12
+        result["prefill_backward"] = {
+            "workload": gi.describe(pc) + " backward (dq, dk, dv)", "value": round(btf, 2),
+            "unit": "TFLOP/s", "ms_per_call": round(bms, 5),
+            "tokens_per_s": round(pc.batch * pc.seq_len / (bms * 1e-3), 1),
+            "pct_of_mfma_peak": round(100 * btf / BF16_MFMA_PEAK_TFLOPS, 2),
+            "roofline": {"kernel": "prefill_bwd_dq + prefill_bwd_dkdv", "bound": "mfma",
+                         "achieved": round(btf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": {k: load_counters(k, "prefill-4k")
+                                     for k in ("prefill_bwd_dq", "prefill_bwd_dkdv")},
+                         "algorithmic_flops": bfl,
+                         "executed_flops": 3.5 * prefill_flops(pc.batch, pc.num_q_heads, pc.seq_len,
+                                                               pc.head_dim)},
         }
 
     if args.calibration_copy:
