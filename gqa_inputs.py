@@ -13,6 +13,9 @@ Workloads (the five shapes the library is measured and checked on):
       drawn uniformly from [1024, 32768] (inclusive), cache capacity 32768
   mqa-128k    MQA long-context decode, bf16: B=4, Hq=16, Hkv=1, d=128, 131072 tokens
   prefill-4k  causal prefill, bf16: B=2, Hq=32, Hkv=8, d=128, N=4096
+  mla-decode  (WIDE_CONFIGS) decode in the absorbed-MLA shape, bf16: B=64,
+      Hq=128 query heads over one cached 576-column row per token (512 latent
+      + 64 rotary), value = the first 512 columns, 4096 tokens, seed 1006
 
 Recipe: seeds 1001..1005 in the order listed above; ``SeedSequence(seed).spawn(4)`` gives
 independent PCG64 streams for (lengths, Q, K, V) in that order; values are
@@ -85,8 +88,47 @@ CONFIGS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class WideConfig:
+    """Decode in the absorbed-MLA shape: Hq query heads over Hkv cached rows
+    of d_k columns, the first d_v of which are also the value."""
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    d_k: int
+    d_v: int
+    max_seq_len: int
+    min_len: int
+    max_len: int
+    seed: int
+    scale_dim: int        # scores are divided by sqrt(scale_dim)
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.scale_dim)
+
+    @property
+    def ragged(self) -> bool:
+        return self.min_len != self.max_len
+
+
+# The MLA decode shape: 128 query heads sharing one 512-column latent row plus
+# a 64-column rotary key (576 cached numbers per token); scores divided by
+# sqrt(128 + 64), the per-head query/key width before absorption.
+WIDE_CONFIGS = {
+    "mla-decode": WideConfig("mla-absorbed-decode-bf16", 64, 128, 1, 576, 512, 4096, 4096, 4096, 1006, 192),
+}
+
+
 def describe(cfg) -> str:
     """One-line workload description used in bench output and test ids."""
+    if isinstance(cfg, WideConfig):
+        lens = (f"T={cfg.max_len}" if not cfg.ragged
+                else f"T~U[{cfg.min_len},{cfg.max_len}] cap={cfg.max_seq_len}")
+        return (f"wide decode {cfg.dtype} B={cfg.batch} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} "
+                f"d_k={cfg.d_k} d_v={cfg.d_v} {lens}")
     if isinstance(cfg, DecodeConfig):
         lens = (f"T={cfg.max_len}" if not cfg.ragged
                 else f"T~U[{cfg.min_len},{cfg.max_len}] cap={cfg.max_seq_len}")
@@ -339,3 +381,44 @@ def make_fp8(inp: DecodeInputs) -> Fp8Inputs:
                 codes[b, kv, int(inp.seq_lens[b]):] = 0x7F
         out += [codes, scales]
     return Fp8Inputs(inp.cfg, inp.q, out[0], out[2], out[1], out[3], inp.seq_lens)
+
+
+# ---------------------------------------------------------------------------
+# Wide shared rows (absorbed-MLA decode)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class WideInputs:
+    cfg: WideConfig
+    q: np.ndarray          # [B, Hq, d_k]          bf16 bits
+    kv_cache: np.ndarray   # [B, Hkv, T_cap, d_k]  bf16 bits; value = first d_v columns
+    seq_lens: np.ndarray   # [B] int32
+
+
+def make_wide(cfg: WideConfig) -> WideInputs:
+    """Streams (lengths, q, cache) of SeedSequence(seed).spawn(4); N(0,1)
+    values rounded to bf16; cache rows past each length are NaN."""
+    r_len, r_q, r_kv, _ = _streams(cfg.seed)
+    if cfg.ragged:
+        lens = r_len.integers(cfg.min_len, cfg.max_len, endpoint=True, size=cfg.batch).astype(np.int32)
+    else:
+        lens = np.full(cfg.batch, cfg.max_len, dtype=np.int32)
+    q = _normals(r_q, (cfg.batch, cfg.num_q_heads, cfg.d_k), "bf16")
+    kv = np.empty((cfg.batch, cfg.num_kv_heads, cfg.max_seq_len, cfg.d_k), dtype=np.uint16)
+    for b in range(cfg.batch):
+        kv[b] = _normals(r_kv, (cfg.num_kv_heads, cfg.max_seq_len, cfg.d_k), "bf16")
+    poison_past_lengths(kv, lens, "bf16")
+    return WideInputs(cfg, q, kv, lens)
+
+
+def small_wide(batch: int, num_q_heads: int, num_kv_heads: int, d_k: int, d_v: int, seq_lens,
+               max_seq_len: int, seed: int, scale_dim: int = 192) -> WideInputs:
+    """Wide-row decode inputs of an arbitrary small shape (given lengths)."""
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    cfg = WideConfig(f"small-wide-{seed}", batch, num_q_heads, num_kv_heads, d_k, d_v, max_seq_len,
+                     int(lens.min()), int(lens.max()), seed, scale_dim)
+    _, r_q, r_kv, _ = _streams(seed)
+    q = _normals(r_q, (batch, num_q_heads, d_k), "bf16")
+    kv = _normals(r_kv, (batch, num_kv_heads, max_seq_len, d_k), "bf16")
+    poison_past_lengths(kv, lens, "bf16")
+    return WideInputs(cfg, q, kv, lens)

@@ -12,7 +12,8 @@ heads explicitly repeated along the query-head axis, in float64:
 * ``kv_math``     the closed forms for KV-cache bytes and decode FLOPs;
 * ``paged``       decode over a paged KV cache (gather, then the plain definition);
 * ``fp8``         decode over an E4M3 cache with per-KV-head scales (dequantise, then decode);
-* ``backward``    gradients of causal prefill (repeat K/V, chain rule per head, sum back).
+* ``backward``    gradients of causal prefill (repeat K/V, chain rule per head, sum back);
+* ``wide``        decode whose cached rows are key and (leading columns) value: the absorbed-MLA shape.
 
 Every function cites the passage of the source pages it follows.  The oracle
 is pinned by tests/test_oracle_pins.py against values the pages print, closed
@@ -31,6 +32,7 @@ from .attention import (  # noqa: F401
 )
 from .paged import gather_pages, decode_paged  # noqa: F401
 from .fp8 import e4m3_value, dequantize, decode_fp8  # noqa: F401
+from .wide import decode_wide  # noqa: F401
 from .backward import (  # noqa: F401
     reduce_kv_heads,
     prefill_causal_backward,

@@ -56,3 +56,16 @@ def test_workload_table():
     assert (c["mqa-128k"].batch, c["mqa-128k"].num_q_heads, c["mqa-128k"].num_kv_heads, c["mqa-128k"].max_seq_len) == (4, 16, 1, 131072)
     assert (c["prefill-4k"].batch, c["prefill-4k"].num_q_heads, c["prefill-4k"].num_kv_heads, c["prefill-4k"].seq_len) == (2, 32, 8, 4096)
     assert [c[k].seed for k in ("tiny-f32", "llama3-8b", "wide-group", "mqa-128k", "prefill-4k")] == [1001, 1002, 1003, 1004, 1005]
+
+
+def test_wide_inputs():
+    cfg = gi.WIDE_CONFIGS["mla-decode"]
+    assert (cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.d_k, cfg.d_v, cfg.max_len, cfg.seed) == \
+        (64, 128, 1, 576, 512, 4096, 1006)
+    assert abs(cfg.scale - 1 / 192 ** 0.5) < 1e-15
+    a = gi.small_wide(2, 8, 1, 576, 512, [40, 7], 48, seed=5)
+    b = gi.small_wide(2, 8, 1, 576, 512, [40, 7], 48, seed=5)
+    assert a.q.shape == (2, 8, 576) and a.kv_cache.shape == (2, 1, 48, 576) and a.q.dtype == np.uint16
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.kv_cache, b.kv_cache)
+    assert np.all(a.kv_cache[1, :, 7:] == gi.BF16_NAN_BITS)
+    assert np.all(np.isfinite(gi.bf16_bits_to_f32(a.kv_cache[1, :, :7])))
