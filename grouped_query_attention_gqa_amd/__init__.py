@@ -26,6 +26,7 @@ __all__ = [
     "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
     "gqa_decode_plan", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
     "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
+    "gqa_decode_wide_plan", "gqa_decode_wide",
     "GQA_F32", "GQA_BF16",
 ]
 
@@ -90,6 +91,10 @@ def load_library():
     lib.gqa_decode_fp8_split.argtypes = lib.gqa_decode_fp8.argtypes
     lib.gqa_prefill_causal.restype = I32
     lib.gqa_prefill_causal.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P]
+    lib.gqa_decode_wide_plan.restype = I32
+    lib.gqa_decode_wide_plan.argtypes = [I32] * 7 + [ctypes.POINTER(I32), ctypes.POINTER(I64)]
+    lib.gqa_decode_wide.restype = I32
+    lib.gqa_decode_wide.argtypes = [P, P, P, P] + [I32] * 6 + [F32, I32, P, I64, P]
     lib.gqa_prefill_backward_workspace.restype = I32
     lib.gqa_prefill_backward_workspace.argtypes = [I32] * 5 + [ctypes.POINTER(I64)]
     lib.gqa_prefill_causal_backward.restype = I32
@@ -373,3 +378,44 @@ def gqa_prefill_causal_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         B, Hq, Hkv, N, d, scale, dt, _ptr(workspace), workspace.numel(), _stream(dev)))
     return dq, dk, dv
+
+
+def gqa_decode_wide_plan(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                         head_dim_qk: int = 576, head_dim_v: int = 512, split_tokens: int = 0):
+    """(token ranges per sequence, workspace bytes) of ``gqa_decode_wide``."""
+    lib = load_library()
+    rng, nbytes = ctypes.c_int32(), ctypes.c_int64()
+    _check("gqa_decode_wide_plan", lib.gqa_decode_wide_plan(
+        batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, max_seq_len, split_tokens,
+        ctypes.byref(rng), ctypes.byref(nbytes)))
+    return rng.value, nbytes.value
+
+
+def gqa_decode_wide(q: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor, head_dim_v: int = 512,
+                    scale: Optional[float] = None, split_tokens: int = 0,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Decode over cached rows that are key and (leading head_dim_v columns)
+    value, the absorbed-MLA shape; returns out [B, Hq, head_dim_v] float32.
+    ``scale`` defaults to 1/sqrt(192), the per-head query/key width of the
+    MLA layer before absorption (128 + 64)."""
+    _require(q.dim() == 3 and kv_cache.dim() == 4, "expected q [B,Hq,dk] and kv_cache [B,Hkv,T,dk]")
+    B, Hq, dk = q.shape
+    B2, Hkv, T, dk2 = kv_cache.shape
+    _require(B == B2 and dk == dk2, "q and kv_cache disagree on batch or head_dim_qk")
+    _require(q.dtype == kv_cache.dtype == torch.bfloat16, "q and kv_cache must be bfloat16")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    dev = _on_gpu(q, kv_cache, seq_lens)
+    scale = 1.0 / math.sqrt(192.0) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hq, head_dim_v), dtype=torch.float32, device=dev)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, head_dim_v), "out must be float32 [B,Hq,dv]")
+    _on_gpu(q, out)
+    if workspace is None:
+        _, nbytes = gqa_decode_wide_plan(B, Hq, Hkv, T, dk, head_dim_v, split_tokens)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _on_gpu(q, workspace)
+    lib = load_library()
+    _check("gqa_decode_wide", lib.gqa_decode_wide(
+        _ptr(q), _ptr(kv_cache), _ptr(seq_lens), _ptr(out), B, Hq, Hkv, dk, head_dim_v, T, scale,
+        split_tokens, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out

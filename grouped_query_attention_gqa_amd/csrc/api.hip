@@ -98,6 +98,42 @@ int64_t backward_workspace_bytes(int32_t batch, int32_t hq, int32_t n) {
   return ((int64_t)batch * hq * n * 8 + 255) / 256 * 256;
 }
 
+// Wide-row decode plan: head blocks of kWideHeadBlock, and with
+// split_tokens == 0 enough token ranges that about 256 workgroups run.
+int32_t make_wide_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d_k, int32_t d_v, int32_t tcap,
+                       int32_t split_tokens, float scale, gqa::WideShape* s) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || tcap < 1) return GQA_ERR_SHAPE;
+  if (d_k != gqa::kWideDK || d_v != gqa::kWideDV) return GQA_ERR_UNSUPPORTED;
+  if (split_tokens < 0 || split_tokens % gqa::kRangeQuantum != 0) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)tcap * d_k * 2 > INT32_MAX) return GQA_ERR_SHAPE;   // 32-bit buffer offsets per cache row
+  if ((int64_t)hq * d_k * 2 > INT32_MAX) return GQA_ERR_SHAPE;
+  const int64_t g = hq / hkv;
+  const int64_t nhb = (g + gqa::kWideHeadBlock - 1) / gqa::kWideHeadBlock;
+  const int64_t units = (int64_t)batch * hkv * nhb;
+  int64_t split = split_tokens;
+  if (split == 0) {
+    const int64_t want = units >= 256 ? 1 : (256 + units - 1) / units;
+    split = (tcap + want - 1) / want;
+    split = (split + gqa::kRangeQuantum - 1) / gqa::kRangeQuantum * gqa::kRangeQuantum;
+  }
+  const int64_t nranges = (tcap + split - 1) / split;
+  const int64_t space = (int64_t)batch * hkv * nranges;
+  const int64_t grid = (space + 7) / 8 * 8 * nhb;
+  if (grid > INT32_MAX || nranges * units * gqa::kWideHeadBlock * gqa::kWideDV > (INT64_MAX / 8))
+    return GQA_ERR_SHAPE;
+  s->batch = batch;
+  s->hq = hq;
+  s->hkv = hkv;
+  s->tcap = tcap;
+  s->nhb = (int)nhb;
+  s->units = (int)units;
+  s->split = (int)split;
+  s->nranges = (int)nranges;
+  s->grid = (int)grid;
+  s->scale = scale;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -347,6 +383,37 @@ int32_t gqa_prefill_causal_backward(const void* q, const void* k, const void* v,
   return hip_status(gqa::launch_prefill_backward(q, k, v, out, lse, dout, dq, dk, dv,
                                                  static_cast<float*>(workspace), s,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int32_t gqa_decode_wide_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                             int32_t head_dim_v, int32_t max_seq_len, int32_t split_tokens,
+                             int32_t* ranges_out, int64_t* workspace_bytes_out) {
+  gqa::WideShape s;
+  const int32_t st = make_wide_plan(batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, max_seq_len,
+                                    split_tokens, 1.f, &s);
+  if (st != GQA_OK) return st;
+  if (ranges_out) *ranges_out = s.nranges;
+  if (workspace_bytes_out) *workspace_bytes_out = gqa::wide_workspace_bytes(s);
+  return GQA_OK;
+}
+
+int32_t gqa_decode_wide(const void* q, const void* kv_cache, const int32_t* seq_lens, float* out,
+                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                        int32_t head_dim_v, int32_t max_seq_len, float scale, int32_t split_tokens,
+                        void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !kv_cache || !seq_lens || !out) return GQA_ERR_NULL;
+  gqa::WideShape s;
+  const int32_t st = make_wide_plan(batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, max_seq_len,
+                                    split_tokens, scale, &s);
+  if (st != GQA_OK) return st;
+  const int64_t need = gqa::wide_workspace_bytes(s);
+  if (need > 0 && !workspace) return GQA_ERR_NULL;
+  if (workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(seq_lens, 4) ||
+      (need > 0 && !aligned(workspace, 16)))
+    return GQA_ERR_ALIGN;
+  return hip_status(gqa::launch_decode_wide(q, kv_cache, seq_lens, out, static_cast<char*>(workspace), s,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

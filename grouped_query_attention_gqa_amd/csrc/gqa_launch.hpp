@@ -57,6 +57,35 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
 hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
                                const DecodeShape& s, hipStream_t stream);
 
+// Wide-row decode (absorbed-MLA shape): cached rows of kWideDK columns whose
+// first kWideDV columns are the value; a workgroup serves kWideHeadBlock
+// query heads of one KV head over one token range.
+constexpr int kWideDK = 576;
+constexpr int kWideDV = 512;
+constexpr int kWideHeadBlock = 64;
+
+struct WideShape {
+  int batch, hq, hkv, tcap;
+  int nhb;       // head blocks per KV head, ceil(g / kWideHeadBlock)
+  int units;     // batch * hkv * nhb
+  int split;     // tokens per range (a multiple of 32)
+  int nranges;   // ceil(tcap / split); 1 means no workspace and no merge
+  int grid;      // workgroups launched (the head blocks of a range share an XCD)
+  float scale;
+};
+
+// Workspace: partial log2-sum-exp [nranges][units][kWideHeadBlock], then
+// normalised partial outputs [nranges][units][kWideHeadBlock][kWideDV].
+inline int64_t wide_lse_bytes(int64_t slots) { return (slots * 4 + 255) / 256 * 256; }
+inline int64_t wide_workspace_bytes(const WideShape& s) {
+  if (s.nranges <= 1) return 0;
+  const int64_t slots = (int64_t)s.nranges * s.units * kWideHeadBlock;
+  return wide_lse_bytes(slots) + slots * kWideDV * 4;
+}
+
+hipError_t launch_decode_wide(const void* q, const void* kv, const int32_t* lens, float* out,
+                              char* workspace, const WideShape& s, hipStream_t stream);
+
 struct PrefillShape {
   int batch, hq, hkv, n, d;
   float scale;

@@ -231,6 +231,46 @@ int32_t gqa_decode_fp8_split(const void* q, const void* k_cache, const void* v_c
                              void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Decode over wide cached rows that are both key and value: the decode shape
+ * of multi-head latent attention with weight absorption, in which all query
+ * heads share one cached latent row per token that serves as the key and,
+ * in its leading columns, as the value (anrans.github.io, "Attention
+ * variants: MQA, GQA, MLA", section "MLA: multi-head latent attention":
+ * 512 latent + 64 rotary-key columns, an MQA with a very large head
+ * dimension).  For query head h and KV head j = h / g:
+ *
+ *     out[h] = sum_t softmax_t(scale * q[h] . row[j, t]) * row[j, t][0 : head_dim_v]
+ *
+ *   q        [batch, num_q_heads, head_dim_qk]               bf16 (absorbed query
+ *            followed by the rotary query)
+ *   kv_cache [batch, num_kv_heads, max_seq_len, head_dim_qk] bf16 (latent row
+ *            followed by the rotary key); rows at or past seq_lens[b] are never read
+ *   seq_lens [batch] int32 on the device, clamped to 0 .. max_seq_len
+ *   out      [batch, num_q_heads, head_dim_v] float32; a sequence with no
+ *            tokens gets zeros
+ *   head_dim_qk must be 576 and head_dim_v 512 (GQA_ERR_UNSUPPORTED
+ *   otherwise); any group size g.  Limits: max_seq_len * 1152 < 2^31.
+ *   split_tokens  0 = automatic token ranges per (sequence, KV head), else a
+ *                 positive multiple of 32 tokens per range
+ *   workspace     partial results when a sequence spans several ranges: at
+ *                 least what gqa_decode_wide_plan reports (may be NULL when
+ *                 that is 0), 16-byte aligned
+ *
+ * gqa_decode_wide_plan reports, for the same arguments, the number of token
+ * ranges per sequence and the workspace bytes.  Errors as gqa_decode.
+ */
+int32_t gqa_decode_wide_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seq_len,
+                             int32_t split_tokens, int32_t* ranges_out,
+                             int64_t* workspace_bytes_out);
+
+int32_t gqa_decode_wide(const void* q, const void* kv_cache, const int32_t* seq_lens, float* out,
+                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim_qk, int32_t head_dim_v, int32_t max_seq_len, float scale,
+                        int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                        void* stream);
+
+/*
  * Causal GQA over a whole prompt (prefill): query row i of head h attends to
  * keys 0..i of KV head h / g (lower-triangular mask broadcast over the
  * group; anrans.github.io, "Kernels do not need to copy the KV heads").

@@ -151,3 +151,30 @@ def test_python_binding_raises_without_gpu_work():
     with pytest.raises(ValueError):
         gqa.gqa_decode(q, torch.zeros(1, 3, 16, 64), torch.zeros(1, 3, 16, 64),
                        torch.zeros(1, dtype=torch.int32))
+
+
+def test_decode_wide_validation(lib):
+    rng, nb = ctypes.c_int32(), ctypes.c_int64()
+    assert lib.gqa_decode_wide_plan(64, 128, 1, 576, 512, 4096, 0, ctypes.byref(rng), ctypes.byref(nb)) == OK
+    assert rng.value >= 2 and nb.value > 0
+    assert lib.gqa_decode_wide_plan(512, 128, 1, 576, 512, 4096, 0, ctypes.byref(rng), ctypes.byref(nb)) == OK
+    assert rng.value == 1 and nb.value == 0                       # enough units: one range, no merge
+    assert lib.gqa_decode_wide_plan(2, 128, 1, 576, 512, 4096, 1024, ctypes.byref(rng), ctypes.byref(nb)) == OK
+    assert rng.value == 4
+    assert lib.gqa_decode_wide_plan(2, 128, 3, 576, 512, 64, 0, None, None) == SHAPE
+
+    def call(q=FAKE, kv=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, B=2, hq=128, hkv=1, dk=576,
+             dv=512, T=4096, split=0):
+        return lib.gqa_decode_wide(q, kv, lens, out, B, hq, hkv, dk, dv, T, 0.07, split, ws, ws_bytes, None)
+    assert call(q=None) == NULL
+    assert call(lens=None) == NULL
+    assert call(ws=None) == NULL              # this shape needs partials
+    assert call(hkv=3) == SHAPE
+    assert call(T=0) == SHAPE
+    assert call(T=1 << 21) == SHAPE           # cache rows past 2 GiB of buffer offsets
+    assert call(dk=512) == UNSUP
+    assert call(dv=256) == UNSUP
+    assert call(split=48) == UNSUP
+    assert call(ws_bytes=1024) == WS
+    assert call(out=MISALIGNED) == ALIGN
+    assert call(lens=ctypes.c_void_p(0x100002)) == ALIGN
