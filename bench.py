@@ -16,7 +16,8 @@ repeated steps.  Kernel durations come from HIP events on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
   python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|
-                  paged-llama3-8b|paged-wide-group|fp8-llama3-8b|fp8-wide-group|fp8-mqa-128k]
+                  paged-llama3-8b|paged-wide-group|fp8-llama3-8b|fp8-wide-group|fp8-mqa-128k|
+                  mla-decode]
                   [--page-size P] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -44,6 +45,7 @@ CSRC = os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc")
 # while their digest is unchanged)
 KERNEL_SOURCES = {
     "decode_split": ("decode.hip", "api.hip", "gqa_device.hpp", "gqa_launch.hpp"),
+    "decode_wide": ("decode_wide.hip", "api.hip", "gqa_device.hpp", "gqa_launch.hpp"),
     "prefill_causal": ("prefill.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
     "prefill_bwd_dq": ("prefill_bwd.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
     "prefill_bwd_dkdv": ("prefill_bwd.hip", "prefill_tiles.hpp", "gqa_device.hpp", "gqa_launch.hpp"),
@@ -136,6 +138,7 @@ COUNTED_KERNELS = {   # kernel-name substring -> sources key
     "prefill_causal_bf16": "prefill_causal",
     "prefill_bwd_dq": "prefill_bwd_dq",
     "prefill_bwd_dkdv": "prefill_bwd_dkdv",
+    "decode_wide_bf16": "decode_wide",
 }
 
 
@@ -223,6 +226,90 @@ def cpu_baseline_decode(inp, budget_s: float, pg=None, fq=None, max_passes: int 
                       f"{t_used:.1f} s of oracle time; value = K/V bytes of the cache / oracle time"}
 
 
+def bench_wide(args, torch, gi, gqa) -> dict:
+    """Decode in the absorbed-MLA shape (gqa_decode_wide): 128 query heads
+    over one 576-column cached row per token whose first 512 columns are the
+    value.  value = cached-row bytes read per step / step time."""
+    cfg = gi.WIDE_CONFIGS["mla-decode"]
+    inp = gi.make_wide(cfg)
+    B, Hq, Hkv, T = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.max_seq_len
+    lens64 = inp.seq_lens.astype(np.int64)
+    kv_bytes = int(lens64.sum()) * Hkv * cfg.d_k * 2
+    flops = int(lens64.sum()) * Hq * (cfg.d_k + cfg.d_v) * 2
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).cuda()
+    kv0 = torch.from_numpy(inp.kv_cache.view(np.int16)).view(torch.bfloat16).cuda()
+    rot = max(2, math.ceil(4 * MALL_BYTES / kv0.numel() / 2))
+    kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    nranges, nbytes = gqa.gqa_decode_wide_plan(B, Hq, Hkv, T, cfg.d_k, cfg.d_v, args.split_tokens)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, cfg.d_v, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        gqa.gqa_decode_wide(q, kvs[i % rot], lens, cfg.d_v, scale=cfg.scale, split_tokens=args.split_tokens,
+                            out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = event_time_ms(step, args.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    alg_bytes = kv_bytes + B * Hq * cfg.d_k * 2
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": gi.describe(cfg), "global_batch": B, "seq_len": T, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim_qk": cfg.d_k, "head_dim_v": cfg.d_v,
+                   "token_ranges": nranges, "kv_rotation_copies": rot, "parallelism": "single-gpu"},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "decode_tflops": round(tf, 2),
+        "pct_of_mfma_peak": round(100 * tf / BF16_MFMA_PEAK_TFLOPS, 2),
+        # intensity (d_k + d_v) * 2 * Hq / (2 d_k) = 242 FLOP/B is below the ridge
+        # 2500 / 8 = 312 FLOP/B, so the roofline's attainable rate is the HBM one
+        "roofline": {"kernel": "decode_wide_bf16 + decode_wide_merge", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_counters("decode_wide", "mla-decode"),
+                     "algorithmic_bytes": alg_bytes, "algorithmic_flops": flops,
+                     "flop_per_byte": round(flops / alg_bytes, 1), "ms_per_launch": round(ms, 5)},
+        "timed_wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_wide(inp, args.cpu_budget)
+    return result
+
+
+def cpu_baseline_wide(inp, budget_s: float, max_passes: int = 4):
+    """The float64 oracle (oracle.decode_wide) on the host, one sequence per
+    call, cycling over the batch until about `budget_s` seconds are spent."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import gqa_inputs as gi
+    import oracle
+    cfg = inp.cfg
+    cores = min(16, len(os.sched_getaffinity(0)))
+    calls, t_used, bytes_done = 0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        while t_used < budget_s and calls < max_passes * cfg.batch:
+            b = calls % cfg.batch
+            q = gi.to_f64(inp.q[b:b + 1], "bf16")
+            kv = gi.to_f64(inp.kv_cache[b:b + 1, :, :int(inp.seq_lens[b])], "bf16")
+            t0 = time.perf_counter()
+            oracle.decode_wide(q, kv, inp.seq_lens[b:b + 1], cfg.d_v, cfg.scale)
+            t_used += time.perf_counter() - t0
+            calls += 1
+            bytes_done += int(inp.seq_lens[b]) * cfg.num_kv_heads * cfg.d_k * 2
+    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{calls} single-sequence oracle.decode_wide calls cycling over the {cfg.batch} sequences "
+                      f"of mla-decode, {t_used:.1f} s of oracle time; value = cached-row bytes / oracle time"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +317,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b",
                     choices=["llama3-8b", "wide-group", "mqa-128k", "paged-llama3-8b", "paged-wide-group",
-                             "fp8-llama3-8b", "fp8-wide-group", "fp8-mqa-128k"])
+                             "fp8-llama3-8b", "fp8-wide-group", "fp8-mqa-128k", "mla-decode"])
     ap.add_argument("--page-size", type=int, default=16, help="tokens per page for the paged-* workloads")
     ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/counters.json from two rocprofv3 --pmc counter CSVs and exit")
@@ -267,6 +354,10 @@ def main():
         sys.exit(2)
     gqa.load_library()   # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+
+    if args.workload == "mla-decode":
+        print(json.dumps(bench_wide(args, torch, gi, gqa)), flush=True)
+        return
 
     paged = args.workload.startswith("paged-")
     fp8 = args.workload.startswith("fp8-")
