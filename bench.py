@@ -166,9 +166,15 @@ def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
 
     ff, fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
     wf, write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    # entries of other workloads recorded earlier are kept; this run's replace theirs
+    try:
+        with open(COUNTERS) as f:
+            kept = json.load(f).get("kernels", {})
+    except (OSError, ValueError):
+        kept = {}
     out = {"calibration": {"kernel": "torch.neg over 64 Mi float32 (256 MiB read + 256 MiB written)",
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
-           "kernels": {}}
+           "kernels": kept}
     for name in fetch:
         wl = "prefill-4k" if name.startswith("prefill") else workload
         fb, wb = fetch[name] * 1024 * ff, write.get(name, 0.0) * 1024 * wf
@@ -176,6 +182,7 @@ def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
             "source_digest": kernel_source_digest(name),
             "fetch_kib_raw": round(fetch[name], 1), "write_kib_raw": round(write.get(name, 0.0), 1),
             "dispatches": [nf[name], nw.get(name, 0)],
+            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
             "fetch_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb)}
     return out
 
@@ -280,6 +287,10 @@ def bench_wide(args, torch, gi, gqa) -> dict:
                      "flop_per_byte": round(flops / alg_bytes, 1), "ms_per_launch": round(ms, 5)},
         "timed_wall_s": round(wall, 4),
     }
+    if args.calibration_copy:
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
+        torch.neg(src, out=torch.empty_like(src))
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_wide(inp, args.cpu_budget)
     return result
