@@ -15,7 +15,11 @@
 // keeps:
 //   Q^T      as MFMA B operands in registers (loaded once),
 //   S^T      [64 keys, 32 rows] = K Q^T in registers,
-//   O^T      [d, 32 rows] fp32 accumulators, rescaled by the online softmax.
+//   O^T      [d, 32 rows] fp32 accumulators.
+// The online softmax keeps a per-row reference point m for the weights
+// exp2(s*scale*log2e - m) and moves it only when a tile's maximum exceeds it
+// by more than 2^8 in weight, so the accumulators are rescaled on few tiles
+// (softmax is shift-invariant, so the result is the same).
 // K/V tiles are double-buffered in LDS and filled by direct global-to-LDS
 // buffer loads (no register staging) while the previous tile is computed;
 // one barrier per tile.  The two stages are separate LDS arrays and the loop
@@ -41,6 +45,7 @@ constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kBN = tiles::kRows;   // keys per tile
 constexpr int kXcds = 8;
 constexpr int kPrefillThreads = tiles::kThreads;
+constexpr float kSlack = 8.f;   // log2 of the largest weight before a rescale
 
 // Per-lane constants of a wavefront: its Q operands and the LDS element
 // offsets of its K and V operands within a tile.
@@ -100,24 +105,14 @@ __device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, 
         sc[kb][r] = t <= lim ? sc[kb][r] : -INFINITY;
       }
   }
+  // Row maximum of the tile in the log2 domain (scale * log2 e folded in).
   float mx = -INFINITY;
-  bf16x8 pb[4];
-  float alpha;
   if (scale_log2 > 0.f) {
-    // max over raw scores; weights exp2(s*c - m) with one FMA each
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = fmaxf(mx, shfl_xor(mx, 32)) * scale_log2;
-    const float m_new = fmaxf(st.m, mx);   // finite: key 0 is in every row's first tile
-    alpha = fast_exp2(st.m - m_new);
-    st.m = m_new;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -m_new));
   } else {
     // zero or negative scale: scale first, then mask-preserving max
 #pragma unroll
@@ -128,13 +123,32 @@ __device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, 
         mx = fmaxf(mx, sc[kb][r]);
       }
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
-    alpha = fast_exp2(st.m - m_new);
+  }
+  // The reference point st.m of the weights moves only when a row's tile
+  // maximum exceeds it by more than kSlack, so weights stay below 2^kSlack
+  // and the O^T accumulators are rescaled only on such (rare) tiles.  Every
+  // row's first tile holds key 0, so st.m is finite from then on.
+  const bool grow = mx > st.m + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float m_new = grow ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
     st.m = m_new;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
+  }
+  bf16x8 pb[4];
+  if (scale_log2 > 0.f) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(sc[kb][r] - m_new);
+      for (int r = 0; r < 16; ++r)
+        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -st.m));
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(sc[kb][r] - st.m);
   }
   // the denominator sums exactly the bf16 weights PV uses (2 per dot)
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -144,12 +158,7 @@ __device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, 
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c][2 * e], pb[c][2 * e + 1]}, ones, ps, false);
-  st.lsum = st.lsum * alpha + ps;
-  // Rescale only when some row's running max moved.
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
-  }
+  st.lsum += ps;
 
   // O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows], four times.  B slots
   // of pb[c]: keys 16c + 4j + (0..3) then 16c + 8 + 4j + (0..3); the V
