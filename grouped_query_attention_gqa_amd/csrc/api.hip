@@ -105,7 +105,7 @@ int32_t make_wide_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d_k, int3
   if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || tcap < 1) return GQA_ERR_SHAPE;
   if (d_k != gqa::kWideDK || d_v != gqa::kWideDV) return GQA_ERR_UNSUPPORTED;
   if (split_tokens < 0 || split_tokens % gqa::kRangeQuantum != 0) return GQA_ERR_UNSUPPORTED;
-  if ((int64_t)tcap * d_k * 2 > INT32_MAX) return GQA_ERR_SHAPE;   // 32-bit buffer offsets per cache row
+  if (((int64_t)tcap + 64) * d_k * 2 > INT32_MAX) return GQA_ERR_SHAPE;   // 32-bit buffer offsets per cache row
   if ((int64_t)hq * d_k * 2 > INT32_MAX) return GQA_ERR_SHAPE;
   const int64_t g = hq / hkv;
   const int64_t nhb = (g + gqa::kWideHeadBlock - 1) / gqa::kWideHeadBlock;

@@ -62,7 +62,7 @@ hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* work
 // query heads of one KV head over one token range.
 constexpr int kWideDK = 576;
 constexpr int kWideDV = 512;
-constexpr int kWideHeadBlock = 128;
+constexpr int kWideHeadBlock = 64;
 
 struct WideShape {
   int batch, hq, hkv, tcap;

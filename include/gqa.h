@@ -249,7 +249,7 @@ int32_t gqa_decode_fp8_split(const void* q, const void* k_cache, const void* v_c
  *   out      [batch, num_q_heads, head_dim_v] float32; a sequence with no
  *            tokens gets zeros
  *   head_dim_qk must be 576 and head_dim_v 512 (GQA_ERR_UNSUPPORTED
- *   otherwise); any group size g.  Limits: max_seq_len * 1152 < 2^31.
+ *   otherwise); any group size g.  Limits: (max_seq_len + 64) * 1152 < 2^31.
  *   split_tokens  0 = automatic token ranges per (sequence, KV head), else a
  *                 positive multiple of 32 tokens per range
  *   workspace     partial results when a sequence spans several ranges: at

@@ -162,6 +162,10 @@ def test_decode_wide_validation(lib):
     assert lib.gqa_decode_wide_plan(2, 128, 1, 576, 512, 4096, 1024, ctypes.byref(rng), ctypes.byref(nb)) == OK
     assert rng.value == 4
     assert lib.gqa_decode_wide_plan(2, 128, 3, 576, 512, 64, 0, None, None) == SHAPE
+    # 32-bit buffer offsets: rows up to max_seq_len + 64 (tiles loaded ahead) must stay below 2^31 bytes
+    t_max = (2 ** 31 - 1) // 1152 - 64
+    assert lib.gqa_decode_wide_plan(2, 128, 1, 576, 512, t_max, 0, None, None) == OK
+    assert lib.gqa_decode_wide_plan(2, 128, 1, 576, 512, t_max + 1, 0, None, None) == SHAPE
 
     def call(q=FAKE, kv=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, B=2, hq=128, hkv=1, dk=576,
              dv=512, T=4096, split=0):
