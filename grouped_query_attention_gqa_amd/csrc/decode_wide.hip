@@ -32,10 +32,13 @@
 // wavefronts accumulate tile it - 1, so the two kinds of MFMA work overlap
 // on every SIMD; two barriers per step.
 // The weights of a range are taken against one fixed maximum per head, the
-// first tile's, so the accumulators never need a rescale; weights up to 2^8
-// are harmless in bf16 and fp32, and a range whose later scores exceed that
-// (not met at ordinary score sizes) is computed a second time against its
-// true maximum.  Token ranges of a unit (sequence, KV head, head block) are
+// first tile's, so the accumulators never need a rescale.  Weights up to
+// 2^32 are harmless in bf16 and fp32 (sums stay far below the fp32 range
+// for any cache length the entry point accepts); a range whose later scores
+// exceed the first tile's maximum by more than that (never at ordinary score
+// sizes) is computed a second time against its true maximum.  The slack is
+// wide on purpose: the workgroup that takes a second pass sets the time of
+// the whole launch.  Token ranges of a unit (sequence, KV head, head block) are
 // merged by their log-sum-exp, as in the narrow decode, when there is more
 // than one.
 // Rows are 72 chunks of 16 bytes; in LDS the low three bits of the chunk
@@ -58,27 +61,25 @@ constexpr int kTok = 32;                          // tokens per tile
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kScoreWaves = 4;                    // wavefronts 0-3 score, 4-7 accumulate values
-constexpr int kQDims = kDK / kScoreWaves;         // 144 contraction columns per score wavefront
-constexpr int kKSteps = kQDims / 16;              // 9 MFMA steps per quarter
+constexpr int kWaveHeads = kWideHeadBlock / kScoreWaves;   // 16 heads per score wavefront
+constexpr int kKSteps = kDK / 32;                 // 18 score MFMAs per 16-token half
 constexpr int kNB = kWideHeadBlock / 32;          // 32-head blocks
 constexpr int kPvCols = kDV / (kWaves - kScoreWaves);   // 128 value columns per value wavefront
 constexpr int kCB = kPvCols / 32;                 // 32-column blocks per value wavefront
-constexpr int kRedHeads = kWideHeadBlock / (kWaves - kScoreWaves);   // heads per value wavefront in the reduction
 constexpr int kChunks = kTok * kCPR;              // 16-byte chunks per tile
-constexpr int kFillThreads = kScoreWaves * 64;    // the score wavefronts load the tiles
+constexpr int kFillThreads = (kWaves - kScoreWaves) * 64;   // the value wavefronts load the tiles
 constexpr int kLoads = kChunks / kFillThreads;    // 16-byte loads per filling thread per tile
-constexpr int kStages = 3;                        // tile ring: loads run two tiles ahead
 // s_waitcnt immediate (gfx9 encoding) for vmcnt <= kLoads with the LDS and
 // export counters left alone: after two tiles' loads have been issued, this
 // waits for the older tile's.
 constexpr int kWaitNewest = (kLoads & 0xF) | ((kLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-constexpr int kXElems = kWideHeadBlock * kTok;    // one quarter's partial scores
 constexpr int kPRow = kTok + 8;                   // bf16 per row of P (80 bytes: 5 chunks)
-constexpr float kLazyMax = 8.f;                   // log2 slack before a second pass
+constexpr int kGroup = 6;                         // K operands read one group ahead of their MFMAs
+constexpr float kLazyMax = 32.f;                  // log2 slack before a second pass
 constexpr int kXcds = 8;
 
-static_assert(kWideHeadBlock == 64 && kNB == 2 && kCB == 4 && kRedHeads == 16, "64-head blocks");
-static_assert(kQDims % 16 == 0, "whole MFMA steps per quarter");
+static_assert(kWideHeadBlock == 64 && kWaveHeads == 16 && kNB == 2 && kCB == 4, "64-head blocks");
+static_assert(kKSteps % 2 == 0 && 2 * kKSteps % kGroup == 0, "score steps in whole groups");
 static_assert(kChunks % kFillThreads == 0, "tile must split evenly over the filling threads");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -97,23 +98,6 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
-}
-
-// Lane exchanges inside quads on the DPP path (no LDS traffic): swap with
-// lane ^ 1, then with lane ^ 2.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
-__device__ __forceinline__ float max4(float x) {
-  x = fmaxf(x, dpp<kDppXor1>(x));
-  return fmaxf(x, dpp<kDppXor2>(x));
-}
-__device__ __forceinline__ float sum4(float x) {
-  x += dpp<kDppXor1>(x);
-  return x + dpp<kDppXor2>(x);
 }
 
 // Barrier over LDS traffic only: waits for this wavefront's LDS accesses,
@@ -135,13 +119,15 @@ struct WideArgs {
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_wide_bf16(WideArgs a) {
-  // three tile stages as separate arrays, so that the compiler can tell a
-  // read of one stage from the loads in flight into another
+  // four tile stages and two weight buffers as separate arrays, so that the
+  // compiler can tell a read of one stage from the loads in flight into
+  // another
   __shared__ __align__(16) __bf16 t0s[kChunks * 8];
   __shared__ __align__(16) __bf16 t1s[kChunks * 8];
   __shared__ __align__(16) __bf16 t2s[kChunks * 8];
-  __shared__ __align__(16) float xs[kScoreWaves * kXElems];    // partial scores [quarter][head][token]
-  __shared__ __align__(16) __bf16 ps[kWideHeadBlock * kPRow];   // weights [head][token]
+  __shared__ __align__(16) __bf16 t3s[kChunks * 8];
+  __shared__ __align__(16) __bf16 p0s[kWideHeadBlock * kPRow];   // weights [head][token], even tiles
+  __shared__ __align__(16) __bf16 p1s[kWideHeadBlock * kPRow];   // odd tiles
   __shared__ float lsum_s[kWideHeadBlock];
 
   // Workgroup -> (space index s = (b, kvh, range), head block hb); the nhb
@@ -167,8 +153,6 @@ void decode_wide_bf16(WideArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool scorer = w < kScoreWaves;
-  const int l32 = lane & 31;
-  const int j = lane >> 5;     // contraction group of the 32x32 operands
 
   if (t_begin >= t_end) {   // nothing to attend in this range (uniform over the workgroup)
     if (a.nranges > 1) {
@@ -183,40 +167,144 @@ void decode_wide_bf16(WideArgs a) {
     }
     return;
   }
+  const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
 
-  // Score role (wavefront w < 4): contraction columns 144 w .. +143 for all
-  // 64 heads.  Q^T B operand (hb2, kk): head 32 hb2 + l32, columns
-  // 144 w + 16 kk + 8 j .. +7.  The two roles run separate loops (with the
-  // same barriers), so Q^T (72 registers) and the value accumulators (128)
-  // share the register file.
-  bf16x8 qb[kNB][kKSteps];
-  f32x16 acc[kCB][kNB];
-  auto load_q = [&]() {
-#pragma unroll
-    for (int hb2 = 0; hb2 < kNB; ++hb2) {
-      const int hl = hbase + 32 * hb2 + l32;
-      const int head = kvh * a.g + min(hl, a.g - 1);
-      const __bf16* qrow = a.q + ((size_t)b * a.hq + head) * kDK + kQDims * w + 8 * j;
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qb[hb2][kk] = load_bf16x8(qrow + 16 * kk);
-    }
+  // The weights of a range are taken against one fixed maximum per head,
+  // the first tile's, so the accumulators are never rescaled.  If a later
+  // tile's maximum exceeded it by more than kLazyMax (weights above 2^32,
+  // which scores of ordinary size never reach) the range is computed again
+  // against the largest maximum, which bounds every weight by 1.  The
+  // decision is workgroup-wide, so both roles take part in the same
+  // barriers; each role keeps to its own code path to the end, so that its
+  // registers are never live in the other's loop.
+  float m_fix = -INFINITY;    // score lanes: the maximum (log2 units) of head c16
+  float m_seen = -INFINITY;   // score lanes: the largest tile maximum met so far
+  float l_run = 0.f;          // score lanes: this lane's share of the sum of weights
+  auto second_pass = [&]() {
+    const bool redo = __syncthreads_or(m_seen > m_fix + kLazyMax);
+    if (redo) m_fix = m_seen;
+    return redo;
   };
-  // K operand of step kk: token l32, logical chunk 18 w + 2 kk + j.  Four
-  // steps later the chunk is 8 further with the same low bits, so four
-  // bases plus 64-element steps cover all nine.  The empty asm hides the
-  // bases' value range so that constants fold into the offset fields.
-  int k_base[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    k_base[p] = l32 * kDK + wide_phys(l32, 2 * (kKSteps * (w & 3) + p) + j) * 8;
-    asm volatile("" : "+v"(k_base[p]));
-  }
-  float* const xw = xs + (w & 3) * kXElems;
 
-  // Value role (wavefront w >= 4): columns 128 (w - 4) .. +127.  V^T operand
-  // (cb, kc): lane l reads column 128 (w - 4) + 32 cb + 16 ((l / 16) % 2) +
-  // ..., rows 16 kc + 8 j + 4 q + (l % 16) / 4 for q = 0, 1 (transposing
-  // reads); the swizzle repeats every 16 rows, so kc is a constant offset.
+  if (scorer) {
+    // Score role: heads 16 w + c16 over all 576 columns on
+    // v_mfma_f32_16x16x32_bf16, S^T[16 tok, 16 heads] per half tile; then
+    // the weights of the 32 tokens are published as P[head][token].
+    const int c16 = lane & 15;   // head within the wavefront (B / D column) and K row
+    const int kg = lane >> 4;    // contraction group
+    const int hw = kWaveHeads * w + c16;   // head within the block
+    const int head = kvh * a.g + min(hbase + hw, a.g - 1);
+    // Q^T B operands: columns 32 kk + 8 kg .. +7 of head `head`.
+    bf16x8 qb[kKSteps];
+    // K operand (tb, kk): token 16 tb + c16, chunk 4 kk + kg; the swizzle
+    // repeats every 16 rows and, for kk two apart, every 8 chunks, so two
+    // bases cover all.  The empty asm hides the bases' value range so that
+    // constants fold into the offset fields.
+    int k_base[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      k_base[p] = c16 * kDK + wide_phys(c16, 4 * p + kg) * 8;
+      asm volatile("" : "+v"(k_base[p]));
+    }
+    const int p_wr = hw * kPRow + 4 * kg;   // P row of this head, tokens 4 kg (+ 16 tb)
+    auto tile = [&](const __bf16* ts, __bf16* pbuf, int t0) {
+      // K operands (kk, tb) in the order n = 2 kk + tb, read in groups of
+      // kGroup one group ahead of the MFMAs that use them (the scheduling
+      // barriers keep the compiler from moving each read next to its use).
+      auto k_op = [&](int n) {
+        const int kk = n >> 1, tb = n & 1;
+        return load_bf16x8(ts + k_base[kk & 1] + 64 * (kk >> 1) + tb * 16 * kDK);
+      };
+      f32x4 sc[2] = {f32x4{}, f32x4{}};
+      bf16x8 kop[2][kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) kop[0][i] = k_op(i);
+#pragma unroll
+      for (int g = 0; g < 2 * kKSteps / kGroup; ++g) {
+        if (g + 1 < 2 * kKSteps / kGroup) {
+#pragma unroll
+          for (int i = 0; i < kGroup; ++i) kop[(g + 1) & 1][i] = k_op(kGroup * (g + 1) + i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+          const int n = kGroup * g + i;
+          sc[n & 1] = mfma16(kop[g & 1][i], qb[n >> 1], sc[n & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // element e of half tb: token t0 + 16 tb + 4 kg + e of head hw
+      float s[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[e] = sc[0][e] * a.scale_log2;
+        s[4 + e] = sc[1][e] * a.scale_log2;
+      }
+      if (t0 + kTok > t_end) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = t0 + 16 * (e >> 2) + 4 * kg + (e & 3) < t_end ? s[e] : -INFINITY;
+      }
+      float mx = max3f(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5]), fmaxf(s[6], s[7]));
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      m_seen = fmaxf(m_seen, mx);
+      m_fix = m_fix == -INFINITY ? mx : m_fix;   // the first tile fixes it (every tile has a token)
+      bf16x4 pw[2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(s[e] - m_fix);
+        l_run += p;
+        pw[e >> 2][e & 3] = (__bf16)p;
+      }
+      *reinterpret_cast<bf16x4*>(pbuf + p_wr) = pw[0];
+      *reinterpret_cast<bf16x4*>(pbuf + p_wr + 16) = pw[1];
+    };
+    // Step it: tile it, weights into buffer it % 2; one barrier per step.
+    auto run = [&]() {
+      {
+        const __bf16* qrow = a.q + ((size_t)b * a.hq + head) * kDK + 8 * kg;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) qb[kk] = load_bf16x8(qrow + 32 * kk);
+      }
+      l_run = 0.f;
+      lds_barrier();   // the first tile has landed
+      for (int it = 0;; it += 4) {
+        tile(t0s, p0s, t_begin + it * kTok);
+        lds_barrier();
+        if (it + 1 >= ntiles) break;
+        tile(t1s, p1s, t_begin + (it + 1) * kTok);
+        lds_barrier();
+        if (it + 2 >= ntiles) break;
+        tile(t2s, p0s, t_begin + (it + 2) * kTok);
+        lds_barrier();
+        if (it + 3 >= ntiles) break;
+        tile(t3s, p1s, t_begin + (it + 3) * kTok);
+        lds_barrier();
+        if (it + 4 >= ntiles) break;
+      }
+    };
+    run();
+    if (second_pass()) run();
+    float l_tot = l_run + shfl_xor(l_run, 16);
+    l_tot += shfl_xor(l_tot, 32);
+    if (kg == 0) {
+      lsum_s[hw] = l_tot;
+      if (a.nranges > 1) a.part_lse[slot0 + hw] = m_fix + __log2f(l_tot);
+    }
+    __syncthreads();
+    return;
+  }
+
+  // Value role (wavefronts 4-7): output columns 128 (w - 4) .. +127 for all
+  // 64 heads, O^T[128, 64] += V^T[128, 32 tok] P^T[32 tok, 64], and the tile
+  // loads.
+  const int wv = w - kScoreWaves;
+  const int l32 = lane & 31;
+  const int j = lane >> 5;   // contraction group of the 32x32 operands
+  // V^T operand (cb, kc): lane l reads column 128 wv + 32 cb + 16 ((l / 16)
+  // % 2) + ..., rows 16 kc + 8 j + 4 q + (l % 16) / 4 for q = 0, 1
+  // (transposing reads); the swizzle repeats every 16 rows, so kc is a
+  // constant offset.
   int v_base[kCB][2];
   {
     const int L = lane & 15;
@@ -226,209 +314,90 @@ void decode_wide_bf16(WideArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int row = 8 * j + 4 * q + (L >> 2);
-        const int col = kPvCols * (w & 3) + 32 * cb + 16 * ch + 4 * (L & 3);
+        const int col = kPvCols * wv + 32 * cb + 16 * ch + 4 * (L & 3);
         v_base[cb][q] = row * kDK + wide_phys(row, col >> 3) * 8 + (col & 7);
         asm volatile("" : "+v"(v_base[cb][q]));
       }
   }
-  auto v_op = [&](const __bf16* ts, int cb, int kc) {
-    return concat(lds_read_tr16(ts + v_base[cb][0] + 16 * kc * kDK),
-                  lds_read_tr16(ts + v_base[cb][1] + 16 * kc * kDK));
-  };
   // P^T operand (nb, kc): head 32 nb + l32, tokens 16 kc + 8 j .. +7.
   const int p_rd = l32 * kPRow + 8 * j;
-
-  // Reduction role (value wavefronts): head hr = 16 (w - 4) + lane / 4,
-  // tokens 8 tq .. 8 tq + 7; partial scores sit in 16-byte units XOR-ed by
-  // (head / 2) mod 8.
-  const int hr = kRedHeads * (w & 3) + (lane >> 2);
-  const int tq = lane & 3;
-  const int xr0 = hr * kTok + ((2 * tq) ^ ((hr >> 1) & 7)) * 4;
-  const int xr1 = hr * kTok + ((2 * tq + 1) ^ ((hr >> 1) & 7)) * 4;
-
-  // Tile fill (score wavefronts): thread tid deposits physical chunks
-  // tid + 256 i of a tile; source offsets are computed once.  Rows past the
-  // range read as zeros without a memory access.
-  const __bf16* kvb = a.kv + ((size_t)b * a.hkv + kvh) * (size_t)a.tcap * kDK;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(kvb, t_end * kDK * 2);
-  int fsrc[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int p = (tid & (kFillThreads - 1)) + kFillThreads * i;
-    const int row = p / kCPR;
-    fsrc[i] = row * kDK * 2 + wide_phys(row, p - row * kCPR) * 16;
-  }
-  auto fill = [&](__bf16* dst, int t0) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + ((w & 3) * 64 + kFillThreads * i) * 8), 16,
-                                               t0 * kDK * 2 + fsrc[i], 0, 0, kCacheDefault);
-  };
-
-  float m_fix = -INFINITY;    // head hr: the maximum (log2 units) the weights are taken against
-  float m_seen = -INFINITY;   // head hr: the largest tile maximum met so far
-  float l_run = 0.f;          // head hr: this lane's share of the sum of weights
-
-  // S^T[32 tok, 64 heads] over this wavefront's quarter of the columns,
-  // published to xs.
-  auto score = [&](const __bf16* ts) {
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-      const bf16x8 kop = load_bf16x8(ts + k_base[kk & 3] + 64 * (kk >> 2));
-      s0 = mfma32(kop, qb[0][kk], s0);
-      s1 = mfma32(kop, qb[1][kk], s1);
-    }
-    // element rr of block hb2: token 8 (rr / 4) + 4 j + rr % 4 of head 32 hb2 + l32
-    auto publish = [&](f32x16 sc, int hb2) {
-      const int hw = 32 * hb2 + l32;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<f32x4*>(xw + hw * kTok + (((2 * r4 + j) ^ ((hw >> 1) & 7)) * 4)) =
-            f32x4{sc[4 * r4], sc[4 * r4 + 1], sc[4 * r4 + 2], sc[4 * r4 + 3]};
-    };
-    publish(s0, 0);
-    publish(s1, 1);
-  };
-  // O^T[128 cols, 64 heads] += V^T[128 cols, 32 tok] P^T[32 tok, 64 heads].
-  auto values = [&](const __bf16* ts) {
+  f32x16 acc[kCB][kNB];
+  auto values = [&](const __bf16* ts, const __bf16* pbuf) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       bf16x8 va[kCB], pb[kNB];
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) va[cb] = v_op(ts, cb, kc);
+      for (int cb = 0; cb < kCB; ++cb)
+        va[cb] = concat(lds_read_tr16(ts + v_base[cb][0] + 16 * kc * kDK),
+                        lds_read_tr16(ts + v_base[cb][1] + 16 * kc * kDK));
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) pb[nb] = load_bf16x8(ps + p_rd + 32 * nb * kPRow + 16 * kc);
+      for (int nb = 0; nb < kNB; ++nb) pb[nb] = load_bf16x8(pbuf + p_rd + 32 * nb * kPRow + 16 * kc);
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) acc[cb][nb] = mfma32(va[cb], pb[nb], acc[cb][nb]);
     }
   };
-  // Sum the four quarters of head hr, tokens 8 tq .. +7, weight them and
-  // publish the weights to ps.
-  auto reduce = [&](int t0) {
-    f32x4 a0 = *reinterpret_cast<const f32x4*>(xs + xr0);
-    f32x4 a1 = *reinterpret_cast<const f32x4*>(xs + xr1);
+  // Tile loads: thread tid - 256 deposits physical chunks (tid - 256) +
+  // 256 i of a tile; source offsets are computed once.  Rows past the range
+  // read as zeros without a memory access.
+  const __bf16* kvb = a.kv + ((size_t)b * a.hkv + kvh) * (size_t)a.tcap * kDK;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(kvb, t_end * kDK * 2);
+  int fsrc[kLoads];
 #pragma unroll
-    for (int d = 1; d < kScoreWaves; ++d) {
-      a0 += *reinterpret_cast<const f32x4*>(xs + d * kXElems + xr0);
-      a1 += *reinterpret_cast<const f32x4*>(xs + d * kXElems + xr1);
-    }
-    float s[8];
+  for (int i = 0; i < kLoads; ++i) {
+    const int p = (tid - kScoreWaves * 64) + kFillThreads * i;
+    const int row = p / kCPR;
+    fsrc[i] = row * kDK * 2 + wide_phys(row, p - row * kCPR) * 16;
+  }
+  auto fill = [&](__bf16* dst, int tile_idx) {
+    const int t0 = min(t_begin + tile_idx * kTok, t_end);   // past the range: zeros
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[e] = a0[e] * a.scale_log2;
-      s[4 + e] = a1[e] * a.scale_log2;
-    }
-    if (t0 + kTok > t_end) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = t0 + 8 * tq + e < t_end ? s[e] : -INFINITY;
-    }
-    const float mx = max4(max3f(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5]), fmaxf(s[6], s[7])));
-    m_seen = fmaxf(m_seen, mx);
-    m_fix = m_fix == -INFINITY ? mx : m_fix;   // the first tile fixes it (every tile has a token)
-    bf16x8 pw;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(s[e] - m_fix);
-      l_run += p;
-      pw[e] = (__bf16)p;
-    }
-    store_bf16x8(ps + hr * kPRow + 8 * tq, pw);
+    for (int i = 0; i < kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + (wv * 64 + kFillThreads * i) * 8), 16,
+                                               t0 * kDK * 2 + fsrc[i], 0, 0, kCacheDefault);
   };
-
-  // Step it: the score wavefronts work on tile it (in `cur`) while the value
-  // wavefronts finish tile it - 1 (in `prev`, with its weights still in ps);
-  // after a barrier the score wavefronts issue the loads of tile it + 2 into
-  // `prev` while the value wavefronts weight tile it.  Both roles execute
-  // the same barriers.
-  const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
-  auto finish_scores = [&](__bf16* prev, int it) {
-    lds_barrier();   // partial scores published; `prev` and ps are free
-    fill(prev, min(t_begin + (it + 2) * kTok, t_end));   // past the range: zeros
-    __builtin_amdgcn_s_waitcnt(kWaitNewest);   // this thread's loads of tile it + 1 have landed
-    lds_barrier();                             // ... everyone's; the weights are published
+  // Step it: loads of tile it + 2, then tile it - 1 (weights in buffer
+  // (it - 1) % 2), then wait for tile it + 1 and the step's barrier.
+  auto step_end = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitNewest);   // this thread's loads of the next tile have landed
+    lds_barrier();                             // ... everyone's; the step's weights are published
   };
-  auto finish_values = [&](int it) {
-    lds_barrier();
-    reduce(t_begin + it * kTok);
-    lds_barrier();
-  };
-  auto run_scores = [&]() {
-    load_q();
-    fill(t0s, t_begin);
-    fill(t1s, t_begin + kTok);
-    __builtin_amdgcn_s_waitcnt(kWaitNewest);
-    lds_barrier();
-    for (int it = 0; it < ntiles; it += kStages) {
-      score(t0s);
-      finish_scores(t2s, it);
-      if (it + 1 >= ntiles) break;
-      score(t1s);
-      finish_scores(t0s, it + 1);
-      if (it + 2 >= ntiles) break;
-      score(t2s);
-      finish_scores(t1s, it + 2);
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // no load into a stage outlives the pass
-  };
-  auto run_values = [&]() {
+  auto run = [&]() {
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) acc[cb][nb] = f32x16{};
-    l_run = 0.f;
-    lds_barrier();        // the first tile has landed
-    finish_values(0);   // step 0: no earlier tile to accumulate
-    // step it accumulates tile it - 1; after the last tile only that remains
-    for (int it = 1;; it += kStages) {
-      values(t0s);
+    fill(t0s, 0);
+    fill(t1s, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitNewest);
+    lds_barrier();   // the first tile has landed
+    fill(t2s, 2);    // step 0: no earlier tile to accumulate
+    step_end();
+    for (int it = 1;; it += 4) {
+      fill(t3s, it + 2);
+      values(t0s, p0s);
       if (it >= ntiles) break;
-      finish_values(it);
-      values(t1s);
+      step_end();
+      fill(t0s, it + 3);
+      values(t1s, p1s);
       if (it + 1 >= ntiles) break;
-      finish_values(it + 1);
-      values(t2s);
+      step_end();
+      fill(t1s, it + 4);
+      values(t2s, p0s);
       if (it + 2 >= ntiles) break;
-      finish_values(it + 2);
+      step_end();
+      fill(t2s, it + 5);
+      values(t3s, p1s);
+      if (it + 3 >= ntiles) break;
+      step_end();
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no load into a stage outlives the pass
   };
-
-  // The accumulators are never rescaled inside the loop.  The first pass
-  // takes the weights against the first tile's maximum; if a later tile's
-  // maximum exceeded it by more than kLazyMax (weights above 2^8, which
-  // scores of ordinary size never reach) the range is computed again against
-  // the largest maximum, which bounds every weight by 1.  The decision is
-  // workgroup-wide, so both roles take part in the same barriers; each role
-  // keeps to its own code path until the end, so that its registers are
-  // never live in the other's loop.
-  auto second_pass = [&]() {
-    const bool redo = __syncthreads_or(m_seen > m_fix + kLazyMax);
-    if (redo) m_fix = m_seen;
-    return redo;
-  };
-  // Denominators of the block's heads, and the range's log-sum-exp.
-  auto publish_sums = [&]() {
-    if (!scorer) {
-      const float l_tot = sum4(l_run);
-      if (tq == 0) {
-        lsum_s[hr] = l_tot;
-        if (a.nranges > 1) a.part_lse[slot0 + hr] = m_fix + __log2f(l_tot);
-      }
-    }
-    __syncthreads();
-  };
-  if (scorer) {
-    run_scores();
-    if (second_pass()) run_scores();
-    publish_sums();
-    return;
-  }
-  run_values();
-  if (second_pass()) run_values();
-  publish_sums();
-  // O^T block (cb, nb): column 128 (w - 4) + 32 cb + 8 (rr / 4) + 4 j + rr % 4 of head 32 nb + l32
+  run();
+  if (second_pass()) run();
+  __syncthreads();   // the score wavefronts publish the denominators
+  // O^T block (cb, nb): column 128 wv + 32 cb + 8 (rr / 4) + 4 j + rr % 4 of head 32 nb + l32
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int hl = hbase + 32 * nb + l32;
@@ -440,7 +409,7 @@ void decode_wide_bf16(WideArgs a) {
     for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<f32x4*>(o + kPvCols * (w & 3) + 32 * cb + 8 * r4 + 4 * j) =
+        *reinterpret_cast<f32x4*>(o + kPvCols * wv + 32 * cb + 8 * r4 + 4 * j) =
             f32x4{acc[cb][nb][4 * r4], acc[cb][nb][4 * r4 + 1], acc[cb][nb][4 * r4 + 2],
                   acc[cb][nb][4 * r4 + 3]} * inv;
   }

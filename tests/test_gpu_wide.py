@@ -75,9 +75,10 @@ def test_forced_ranges_merge(split):
 
 def test_late_large_score_second_pass():
     """A token well after the first tile whose score exceeds every earlier
-    one by far (more than 2^8 in weight): the kernel must recompute the range
-    against the true maximum.  Checked against the oracle, whose output is
-    then dominated by that token."""
+    one by far (about 2^84 in weight for head 0, beyond the kernel's 2^32
+    slack): the kernel must recompute the range against the true maximum.
+    Checked against the oracle, whose output is then dominated by that
+    token."""
     need_gpu()
     inp = gi.small_wide(1, 64, 1, DK, DV, [200], 224, seed=617)
     q = gi.bf16_bits_to_f32(inp.q[0, 0])
