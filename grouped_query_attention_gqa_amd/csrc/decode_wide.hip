@@ -178,7 +178,7 @@ void decode_wide_bf16(WideArgs a) {
   // barriers; each role keeps to its own code path to the end, so that its
   // registers are never live in the other's loop.
   float m_fix = -INFINITY;    // score lanes: the maximum (log2 units) of head c16
-  float m_seen = -INFINITY;   // score lanes: the largest tile maximum met so far
+  float m_seen = -INFINITY;   // score lanes: the largest score met so far (this lane's, then the head's)
   float l_run = 0.f;          // score lanes: this lane's share of the sum of weights
   auto second_pass = [&]() {
     const bool redo = __syncthreads_or(m_seen > m_fix + kLazyMax);
@@ -207,7 +207,7 @@ void decode_wide_bf16(WideArgs a) {
       asm volatile("" : "+v"(k_base[p]));
     }
     const int p_wr = hw * kPRow + 4 * kg;   // P row of this head, tokens 4 kg (+ 16 tb)
-    auto tile = [&](const __bf16* ts, __bf16* pbuf, int t0) {
+    auto tile = [&](const __bf16* ts, __bf16* pbuf, int t0, bool first) {
       // K operands (kk, tb) in the order n = 2 kk + tb, read in groups of
       // kGroup one group ahead of the MFMAs that use them (the scheduling
       // barriers keep the compiler from moving each read next to its use).
@@ -244,11 +244,15 @@ void decode_wide_bf16(WideArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = t0 + 16 * (e >> 2) + 4 * kg + (e & 3) < t_end ? s[e] : -INFINITY;
       }
-      float mx = max3f(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5]), fmaxf(s[6], s[7]));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      // Only the first tile of a pass needs the head's maximum across lanes
+      // (it fixes m_fix); later tiles only track this lane's own maximum,
+      // which is combined across lanes once, at the end of the pass.
+      const float mx = max3f(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5]), fmaxf(s[6], s[7]));
       m_seen = fmaxf(m_seen, mx);
-      m_fix = m_fix == -INFINITY ? mx : m_fix;   // the first tile fixes it (every tile has a token)
+      if (first) {
+        const float mh = fmaxf(mx, shfl_xor(mx, 16));
+        m_fix = fmaxf(mh, shfl_xor(mh, 32));   // finite: the first tile holds a token
+      }
       bf16x4 pw[2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -260,7 +264,9 @@ void decode_wide_bf16(WideArgs a) {
       *reinterpret_cast<bf16x4*>(pbuf + p_wr + 16) = pw[1];
     };
     // Step it: tile it, weights into buffer it % 2; one barrier per step.
-    auto run = [&]() {
+    // fix_max: the pass takes m_fix from its first tile (the first pass);
+    // the second pass keeps the true maximum found by the first.
+    auto run = [&](bool fix_max) {
       {
         const __bf16* qrow = a.q + ((size_t)b * a.hq + head) * kDK + 8 * kg;
 #pragma unroll
@@ -269,22 +275,28 @@ void decode_wide_bf16(WideArgs a) {
       l_run = 0.f;
       lds_barrier();   // the first tile has landed
       for (int it = 0;; it += 4) {
-        tile(t0s, p0s, t_begin + it * kTok);
+        tile(t0s, p0s, t_begin + it * kTok, fix_max && it == 0);
         lds_barrier();
         if (it + 1 >= ntiles) break;
-        tile(t1s, p1s, t_begin + (it + 1) * kTok);
+        tile(t1s, p1s, t_begin + (it + 1) * kTok, false);
         lds_barrier();
         if (it + 2 >= ntiles) break;
-        tile(t2s, p0s, t_begin + (it + 2) * kTok);
+        tile(t2s, p0s, t_begin + (it + 2) * kTok, false);
         lds_barrier();
         if (it + 3 >= ntiles) break;
-        tile(t3s, p1s, t_begin + (it + 3) * kTok);
+        tile(t3s, p1s, t_begin + (it + 3) * kTok, false);
         lds_barrier();
         if (it + 4 >= ntiles) break;
       }
     };
-    run();
-    if (second_pass()) run();
+    // m_seen of a head: the largest of its four lanes' maxima
+    auto head_seen = [&]() {
+      const float m = fmaxf(m_seen, shfl_xor(m_seen, 16));
+      m_seen = fmaxf(m, shfl_xor(m, 32));
+    };
+    run(true);
+    head_seen();
+    if (second_pass()) run(false);
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
     if (kg == 0) {
