@@ -20,11 +20,17 @@
 // exp2(s*scale*log2e - m) and moves it only when a tile's maximum exceeds it
 // by more than 2^8 in weight, so the accumulators are rescaled on few tiles
 // (softmax is shift-invariant, so the result is the same).
-// K/V tiles are double-buffered in LDS and filled by direct global-to-LDS
-// buffer loads (no register staging) while the previous tile is computed;
-// one barrier per tile.  The two stages are separate LDS arrays and the loop
-// is unrolled by two, so the compiler can see that reading one stage does not
-// alias the loads in flight into the other.  Tiles are stored in 16-byte
+// The tile loop is software-pipelined within each wavefront: step it issues
+// the score MFMAs of tile it + 1 and computes the weights of tile it between
+// them (a branch-free block whose groups are fenced so that the compiler
+// keeps the interleave), so the softmax arithmetic runs while the matrix
+// core works; then tile it is accumulated.  K and V have two LDS stages
+// each, filled by direct global-to-LDS buffer loads (no register staging):
+// step it reads K(it + 1) and V(it) and loads K(it + 2) and V(it + 1) into
+// the stages the previous step finished with, so one barrier per step
+// suffices.  The stages are separate LDS arrays and the loop is unrolled by
+// two, so the compiler can see that reading one stage does not alias the
+// loads in flight into another.  Tiles are stored in 16-byte
 // chunks with the chunk index XOR-ed by a rotation of the key index, which
 // keeps both the K reads (ds_read_b128, 16 keys x one chunk per 16 lanes)
 // and the transposing V reads (ds_read_b64_tr_b16, 4 keys x 2 chunks per 16
@@ -46,129 +52,145 @@ constexpr int kBN = tiles::kRows;   // keys per tile
 constexpr int kXcds = 8;
 constexpr int kPrefillThreads = tiles::kThreads;
 constexpr float kSlack = 8.f;   // log2 of the largest weight before a rescale
+constexpr int kSchedMfma = 0x8;          // sched_group_barrier instruction classes
+constexpr int kSchedValu = 0x2 | 0x400;  // VALU, transcendental included
+constexpr int kSchedDsRead = 0x100;
 
 // Per-lane constants of a wavefront: its Q operands and the LDS element
-// offsets of its K and V operands within a tile.
+// offsets of its K and V operands within a tile.  The tile swizzle repeats
+// every 16 rows, so key block kb (32 rows) and 16-key chunk c are constant
+// offsets (32 kb D and 16 c D) from the bases kept here.
 template <int D>
 struct Lane {
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
-  bf16x8 qb[KSTEPS];     // Q^T B operands: q[pos][16kk + 8j .. +7]
-  int k_rd[2][KSTEPS];   // K: key 32*kb + row, logical chunk 2kk + j
-  int v_rd[4][DB];       // V (transposed): key 16c + 4j + L/4, column 32db + dlo + 4(L%4)
-  int v_dx[4][DB];       // offset correction of the same column 8 keys later
+  bf16x8 qb[KSTEPS];   // Q^T B operands: q[pos][16kk + 8j .. +7]
+  int k_rd[KSTEPS];    // K: key row (of key block 0), logical chunk 2kk + j
+  int v_rd[DB];        // V (transposed), chunk 0: key 4j + L/4, column 32db + dlo + 4(L%4)
+  int v_dx[DB];        // offset correction of the same column 8 keys later
 };
 
 // Online-softmax state of a wavefront's 32 query rows.
 template <int D>
 struct RowState {
-  float m, lsum;              // running max (log2 domain) and this lane's share of the sum
+  float m, lsum;              // reference point (log2 domain) and this lane's share of the sum
   f32x16 acc[D / 32];         // O^T[d, rows]
 };
 
+// S^T[64 keys, 32 rows] = K Q^T of one tile, as two 32-key blocks.
 template <int D>
-__device__ __forceinline__ void attend_tile(const __bf16* ks, const __bf16* vs, const Lane<D>& ln,
-                                            RowState<D>& st, int t0, int pos0, int pos, int n,
-                                            int j, float scale_log2) {
+__device__ __forceinline__ void scores(const __bf16* ks, const Lane<D>& ln, f32x16 (&sc)[2]) {
   constexpr int KSTEPS = Lane<D>::KSTEPS;
-  constexpr int DB = Lane<D>::DB;
-  // All K operands of the tile are read before the first MFMA so the LDS
-  // latency is paid once, not once per step.
-  bf16x8 ka[KSTEPS][2];
+  sc[0] = f32x16{};
+  sc[1] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ka[kk][kb] = load_bf16x8(ks + ln.k_rd[kb][kk]);
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 sc[2] = {f32x16{}, f32x16{}};
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(load_bf16x8(ks + ln.k_rd[kk] + 32 * kb * D), ln.qb[kk], sc[kb]);
+}
+
+// Keys after the row (and past the end) become -inf, by a select, in a tile
+// that crosses the diagonal.  sc[kb][r] is the score of key t0 + 32kb +
+// 8(r/4) + 4j + r%4 for query row `pos`.
+__device__ __forceinline__ void mask_scores(f32x16 (&sc)[2], int t0, int pos, int n, int j) {
+  const int lim = min(pos, n - 1);
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(ka[kk][kb], ln.qb[kk], sc[kb]);
-  // The first V operands load while the softmax runs.
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
+      sc[kb][r] = t <= lim ? sc[kb][r] : -INFINITY;
+    }
+}
+
+// One pipelined step's arithmetic in one branch-free block: the scores of
+// the next tile (K reads and MFMAs into sn) and the weights of this one (sc
+// -> bf16 P^T as four B operands: key chunk c holds keys 16c + 4j + 0..3,
+// then 16c + 8 + 4j + 0..3).  It is written as KSTEPS groups fenced by
+// scheduling barriers: group kk issues the K reads of step kk + 1, the two
+// MFMAs of step kk and a slice of the weights' arithmetic, so the weights
+// are computed while the matrix core runs and the register footprint stays
+// that of one step.  The reference point st.m moves only when a row's tile
+// maximum exceeds it by more than kSlack; the accumulators' rescale by
+// alpha, when that happened in some row (any_grow), is left to the caller.
+// mult > 0 multiplies the raw scores into the log2 domain (scale * log2 e,
+// folded into one FMA per weight, so a positive factor keeps the maximum
+// the maximum); the caller passes scores already scaled and mult = 1 for a
+// zero or negative scale.
+template <int D>
+__device__ __forceinline__ void scores_and_weights(const __bf16* kn, const Lane<D>& ln, f32x16 (&sn)[2],
+                                                   const f32x16 (&sc)[2], RowState<D>& st, bf16x8 (&pb)[4],
+                                                   float& alpha, bool& any_grow, float mult) {
+  constexpr int KSTEPS = Lane<D>::KSTEPS;
+  constexpr int kPerGroup = (32 + KSTEPS - 3) / (KSTEPS - 2);   // weights per group after the two max groups
+  static_assert(kPerGroup % 2 == 0, "weights pair up for the row sums");
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+  bf16x8 kop[2][2];
+  kop[0][0] = load_bf16x8(kn + ln.k_rd[0]);
+  kop[0][1] = load_bf16x8(kn + ln.k_rd[0] + 32 * D);
+  float mx = -INFINITY, m_new = 0.f;
+  float ps = 0.f;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    if (kk + 1 < KSTEPS) {
+      kop[(kk + 1) & 1][0] = load_bf16x8(kn + ln.k_rd[kk + 1]);
+      kop[(kk + 1) & 1][1] = load_bf16x8(kn + ln.k_rd[kk + 1] + 32 * D);
+    }
+    sn[0] = mfma32(kop[kk & 1][0], ln.qb[kk], sn[0]);
+    sn[1] = mfma32(kop[kk & 1][1], ln.qb[kk], sn[1]);
+    if (kk < 2) {
+      // the row maximum: key block kk
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
+      if (kk == 1) {
+        // rows pair lanes l and l + 32: swap halves on the VALU instead of a shuffle through LDS
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * mult;
+        // every row's first tile holds key 0, so st.m is finite from then on
+        const bool grow = mx > st.m + kSlack;
+        m_new = grow ? mx : st.m;
+        alpha = fast_exp2(st.m - m_new);
+        any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+        st.m = m_new;
+      }
+    } else {
+      // weights e0 .. e0 + kPerGroup - 1 of the 32 (element e: block e / 16, register e % 16)
+      const int e0 = (kk - 2) * kPerGroup;
+#pragma unroll
+      for (int e = e0; e < e0 + kPerGroup && e < 32; ++e) {
+        float pe = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], mult, -m_new));
+        asm volatile("" : "+v"(pe));   // keeps the weight in this group (not sunk to its use)
+        pb[e >> 3][e & 7] = (__bf16)pe;
+      }
+      // the denominator sums exactly the bf16 weights PV uses (2 per dot)
+#pragma unroll
+      for (int e = e0; e < e0 + kPerGroup && e < 32; e += 2)
+        ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]}, ones, ps, false);
+      asm volatile("" : "+v"(ps));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.lsum = st.lsum * alpha + ps;
+}
+
+// O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows] over the tile's four
+// key chunks; the V operands of the next chunk load during this chunk's
+// MFMAs.
+template <int D>
+__device__ __forceinline__ void accumulate(const __bf16* vs, const Lane<D>& ln, const bf16x8 (&pb)[4],
+                                           RowState<D>& st) {
+  constexpr int DB = D / 32;
   bf16x8 va[2][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    va[0][db] = tiles::read_tr<D>(vs, ln.v_rd[0][db], ln.v_dx[0][db]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // sc[kb][r] = raw score of key t0 + 32*kb + 8*(r/4) + 4*j + r%4, query row
-  // `pos`.  Keys after the row (and past the end) become -inf, by a select,
-  // only in tiles that cross the diagonal.
-  if (t0 + kBN > pos0 || t0 + kBN > n) {
-    const int lim = min(pos, n - 1);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
-        sc[kb][r] = t <= lim ? sc[kb][r] : -INFINITY;
-      }
-  }
-  // Row maximum of the tile in the log2 domain (scale * log2 e folded in).
-  float mx = -INFINITY;
-  if (scale_log2 > 0.f) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * scale_log2;
-  } else {
-    // zero or negative scale: scale first, then mask-preserving max
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[kb][r] = sc[kb][r] == -INFINITY ? -INFINITY : sc[kb][r] * scale_log2;
-        mx = fmaxf(mx, sc[kb][r]);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-  }
-  // The reference point st.m of the weights moves only when a row's tile
-  // maximum exceeds it by more than kSlack, so weights stay below 2^kSlack
-  // and the O^T accumulators are rescaled only on such (rare) tiles.  Every
-  // row's first tile holds key 0, so st.m is finite from then on.
-  const bool grow = mx > st.m + kSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    const float m_new = grow ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);
-    st.m = m_new;
-    st.lsum *= alpha;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
-  }
-  bf16x8 pb[4];
-  if (scale_log2 > 0.f) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -st.m));
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(sc[kb][r] - st.m);
-  }
-  // the denominator sums exactly the bf16 weights PV uses (2 per dot)
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  float ps = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c][2 * e], pb[c][2 * e + 1]}, ones, ps, false);
-  st.lsum += ps;
-
-  // O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows], four times.  B slots
-  // of pb[c]: keys 16c + 4j + (0..3) then 16c + 8 + 4j + (0..3); the V
-  // operands of the next key chunk load during this chunk's MFMAs.
+  for (int db = 0; db < DB; ++db) va[0][db] = tiles::read_tr<D>(vs, ln.v_rd[db], ln.v_dx[db]);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (c + 1 < 4) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        va[(c + 1) & 1][db] = tiles::read_tr<D>(vs, ln.v_rd[c + 1][db], ln.v_dx[c + 1][db]);
+        va[(c + 1) & 1][db] = tiles::read_tr<D>(vs + 16 * (c + 1) * D, ln.v_rd[db], ln.v_dx[db]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -186,8 +208,8 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   constexpr int DB = D / 32;
   constexpr int TILE = kBN * D;         // bf16 elements per K or V tile
   __shared__ __align__(16) __bf16 k0s[TILE];
-  __shared__ __align__(16) __bf16 v0s[TILE];
   __shared__ __align__(16) __bf16 k1s[TILE];
+  __shared__ __align__(16) __bf16 v0s[TILE];
   __shared__ __align__(16) __bf16 v1s[TILE];
 
   // Workgroup -> (unit = (b, kvh, head block), q-tile), heaviest tiles first.
@@ -226,13 +248,15 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) ln.qb[kk] = load_bf16x8(qrow + 16 * kk + 8 * j);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      ln.k_rd[kk] = tiles::row_offset<D>(row, 2 * kk + j);
+      asm volatile("" : "+v"(ln.k_rd[kk]));
+    }
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) ln.k_rd[kb][kk] = tiles::row_offset<D>(32 * kb + row, 2 * kk + j);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, ln.v_rd[c][db], ln.v_dx[c][db]);
+    for (int db = 0; db < DB; ++db) {
+      tiles::tr_offsets<D>(lane, 0, db, ln.v_rd[db], ln.v_dx[db]);
+      asm volatile("" : "+v"(ln.v_rd[db]));
+    }
   }
 
   // K/V of this (sequence, KV head); rows >= n read as zeros.
@@ -250,23 +274,59 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int kv_hi = min(n, q0 + mq);       // keys any row of the workgroup needs
   const int wave_hi = min(n, pos0 + 32);   // keys this wavefront needs
   const int ntiles = (kv_hi + kBN - 1) / kBN;
+  const int nt_w = (wave_hi + kBN - 1) / kBN;   // tiles this wavefront needs (a prefix, at least one)
 
-  fill.issue2(k0s, rk, v0s, rv, w, 0);
+  // Software pipeline over the tiles: in step it the scores of tile it + 1
+  // are issued on the matrix cores first, and the weights of tile it (whose
+  // scores the previous step produced) are computed while those MFMAs run;
+  // then tile it is accumulated.  K and V have two LDS stages each: step it
+  // reads K(it + 1) and V(it) and loads K(it + 2) and V(it + 1) into the
+  // stages that step it - 1 finished with, so one barrier per step suffices.
+  fill.issue(k0s, rk, w, 0);
+  fill.issue(v0s, rv, w, 0);
+  if (ntiles > 1) fill.issue(k1s, rk, w, kBN);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sc[2];
+  scores<D>(k0s, ln, sc);   // tile 0: every row needs key 0
+  __syncthreads();          // k0s is free for K(2)
+
+  // One step; kn/vc hold K(it + 1)/V(it), kf/vf receive K(it + 2)/V(it + 1).
+  auto step = [&](const __bf16* kn, const __bf16* vc, __bf16* kf, __bf16* vf, int it) {
+    if (it + 2 < ntiles) fill.issue(kf, rk, w, (it + 2) * kBN);
+    if (it + 1 < ntiles) fill.issue(vf, rv, w, (it + 1) * kBN);
+    f32x16 sn[2];
+    if (it < nt_w) {
+      const int t0 = it * kBN;
+      if (t0 + kBN > pos0 || t0 + kBN > n) mask_scores(sc, t0, pos, n, j);
+      if (scale_log2 <= 0.f) {
+        // zero or negative scale: scale first, keeping masked keys at -inf
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][r] = sc[kb][r] == -INFINITY ? -INFINITY : sc[kb][r] * scale_log2;
+      }
+      // (after the wavefront's last tile the scores of the next are computed
+      // but never used: reading a stage that holds no tile is harmless)
+      bf16x8 pb[4];
+      float alpha;
+      bool any_grow;
+      scores_and_weights<D>(kn, ln, sn, sc, st, pb, alpha, any_grow, scale_log2 > 0.f ? scale_log2 : 1.f);
+      if (any_grow) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
+      }
+      accumulate<D>(vc, ln, pb, st);
+    }
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads for the next step have landed
+    __syncthreads();                 // ... everyone's, and the stages read here are free again
+  };
   for (int it = 0; it < ntiles; it += 2) {
-    // stage 0 holds tile it
-    if (it + 1 < ntiles) fill.issue2(k1s, rk, v1s, rv, w, (it + 1) * kBN);
-    if (it * kBN < wave_hi) attend_tile<D>(k0s, v0s, ln, st, it * kBN, pos0, pos, n, j, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile have landed
-    __syncthreads();                 // ... everyone's, and everyone is done with stage 0
+    step(k1s, v0s, k0s, v1s, it);
     if (it + 1 >= ntiles) break;
-    // stage 1 holds tile it + 1
-    if (it + 2 < ntiles) fill.issue2(k0s, rk, v0s, rv, w, (it + 2) * kBN);
-    if ((it + 1) * kBN < wave_hi)
-      attend_tile<D>(k1s, v1s, ln, st, (it + 1) * kBN, pos0, pos, n, j, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    step(k0s, v1s, k1s, v0s, it + 1);
   }
 
   const float lsum = st.lsum + shfl_xor(st.lsum, 32);
