@@ -52,9 +52,6 @@ constexpr int kBN = tiles::kRows;   // keys per tile
 constexpr int kXcds = 8;
 constexpr int kPrefillThreads = tiles::kThreads;
 constexpr float kSlack = 8.f;   // log2 of the largest weight before a rescale
-constexpr int kSchedMfma = 0x8;          // sched_group_barrier instruction classes
-constexpr int kSchedValu = 0x2 | 0x400;  // VALU, transcendental included
-constexpr int kSchedDsRead = 0x100;
 
 // Per-lane constants of a wavefront: its Q operands and the LDS element
 // offsets of its K and V operands within a tile.  The tile swizzle repeats
