@@ -617,10 +617,12 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the segment partials: one workgroup per (query head,
 // sequence).  Threads hold 4 head coordinates each; D/4 threads cover one
-// partial row and the 256 threads walk 1024/D rows at a time, so many loads
-// are in flight; the row groups are then combined through LDS.  Units
-// written directly by a single segment are skipped; empty sequences get
-// zeros.
+// partial row, so the 256 threads form 1024/D row groups.  A round loads
+// eight rows per thread, each row's lse and output together, so one round
+// trip to memory serves up to 8192/D segments.  Every row group keeps its
+// own running maximum (online softmax over the partials); the groups are
+// then combined through LDS against the largest.  Units written directly by
+// a single segment are skipped; empty sequences get zeros.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
 
@@ -630,10 +632,11 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
                   const int* __restrict__ unit_info, const int32_t* __restrict__ lens,
                   float* __restrict__ out, int hq, int hkv, int g, int nhb, int tcap) {
   constexpr int C4 = D / 4;                  // float4 columns per row
-  constexpr int ROWS = kMergeThreads / C4;   // partial rows read concurrently
-  __shared__ float red[kMergeThreads / 64];
+  constexpr int ROWS = kMergeThreads / C4;   // row groups
+  constexpr int U = 8;                       // rows per thread per round
   __shared__ f32x4 racc[ROWS][C4];
   __shared__ float rl[ROWS];
+  __shared__ float rm[ROWS];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -650,37 +653,54 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
   const int ns = unit_info[2 * unit + 1];
   if (ns <= 1) return;   // written directly by its only segment
 
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += kMergeThreads)
-    mx = fmaxf(mx, part_lse[((size_t)base + s) * kDecodeHeadBlock + hl]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
-
+  // Row group sr: segments sr, sr + ROWS, ...  Every segment holds at least
+  // one token, so its lse is finite; rows past ns are padding, loaded from
+  // the last segment and given lse -inf (weight 0).
   const int c4 = tid % C4;
   const int sr = tid / C4;
-  float L = 0.f;
+  float m = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = sr; s < ns; s += ROWS) {
-    const size_t row = ((size_t)base + s) * kDecodeHeadBlock + hl;
-    const float wt = fast_exp2(part_lse[row] - M);
-    L += wt;
-    acc += wt * reinterpret_cast<const f32x4*>(part_o + row * D)[c4];
+  for (int s0 = sr; s0 < ns; s0 += U * ROWS) {
+    float lr[U];
+    f32x4 ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * ROWS;
+      const size_t row = ((size_t)base + min(s, ns - 1)) * kDecodeHeadBlock + hl;
+      lr[u] = s < ns ? part_lse[row] : -INFINITY;
+      ov[u] = reinterpret_cast<const f32x4*>(part_o + row * D)[c4];
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, lr[u]);   // finite: lr[0] is
+    const float rs = fast_exp2(m - mn);
+    L *= rs;
+    acc *= rs;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wt = fast_exp2(lr[u] - mn);
+      L += wt;
+      acc += wt * ov[u];
+    }
+    m = mn;
   }
   racc[sr][c4] = acc;
-  if (c4 == 0) rl[sr] = L;
+  if (c4 == 0) {
+    rl[sr] = L;
+    rm[sr] = m;   // -inf for a group with no rows: weight 0 below
+  }
   __syncthreads();
   if (sr == 0) {
-    float Lt = rl[0];
-    f32x4 a = racc[0][c4];
+    float M = rm[0];
 #pragma unroll
-    for (int rr = 1; rr < ROWS; ++rr) {
-      Lt += rl[rr];
-      a += racc[rr][c4];
+    for (int rr = 1; rr < ROWS; ++rr) M = fmaxf(M, rm[rr]);
+    float Lt = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr) {
+      const float wt = fast_exp2(rm[rr] - M);
+      Lt += wt * rl[rr];
+      a += wt * racc[rr][c4];
     }
     reinterpret_cast<f32x4*>(o)[c4] = a / Lt;
   }

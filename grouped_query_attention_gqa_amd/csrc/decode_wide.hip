@@ -442,22 +442,36 @@ void decode_wide_merge(const float* __restrict__ part_o, const float* __restrict
   const int unit = (b * hkv + kvh) * nhb + hb;
   const int lane_slot = hl - hb * kWideHeadBlock;
   const int c4 = threadIdx.x;
-  float mx = -INFINITY;
-  for (int r = 0; r < nranges; ++r)
-    mx = fmaxf(mx, part_lse[((size_t)r * units + unit) * kWideHeadBlock + lane_slot]);
+  // Four ranges per round, each range's lse and output loaded together (one
+  // round trip for up to four ranges), combined online against the running
+  // maximum.  The output of an empty range is never written, so it is
+  // selected away rather than multiplied by its zero weight.
+  float mx = -INFINITY, den = 0.f;
   f32x4 acc = f32x4{};
-  if (mx != -INFINITY) {
-    float den = 0.f;
-    for (int r = 0; r < nranges; ++r) {
-      const size_t slot = ((size_t)r * units + unit) * kWideHeadBlock + lane_slot;
-      const float lr = part_lse[slot];
-      if (lr == -INFINITY) continue;
-      const float wgt = fast_exp2(lr - mx);
-      den += wgt;
-      acc += wgt * *reinterpret_cast<const f32x4*>(part_o + slot * kDV + 4 * c4);
+  for (int r0 = 0; r0 < nranges; r0 += 4) {
+    float lr[4];
+    f32x4 ov[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + u;
+      const size_t slot = ((size_t)min(r, nranges - 1) * units + unit) * kWideHeadBlock + lane_slot;
+      lr[u] = r < nranges ? part_lse[slot] : -INFINITY;
+      ov[u] = *reinterpret_cast<const f32x4*>(part_o + slot * kDV + 4 * c4);
     }
-    acc *= 1.f / den;
+    const float mn = fmaxf(mx, fmaxf(fmaxf(lr[0], lr[1]), fmaxf(lr[2], lr[3])));
+    if (mn == -INFINITY) continue;   // no tokens so far
+    const float rs = fast_exp2(mx - mn);
+    den *= rs;
+    acc *= rs;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = fast_exp2(lr[u] - mn);
+      den += wgt;
+      acc += lr[u] == -INFINITY ? f32x4{} : wgt * ov[u];
+    }
+    mx = mn;
   }
+  if (mx != -INFINITY) acc *= 1.f / den;
   *reinterpret_cast<f32x4*>(out + ((size_t)b * hq + h) * kDV + 4 * c4) = acc;
 }
 
