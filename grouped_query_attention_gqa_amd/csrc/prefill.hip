@@ -289,9 +289,14 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   __syncthreads();          // k0s is free for K(2)
 
   // One step; kn/vc hold K(it + 1)/V(it), kf/vf receive K(it + 2)/V(it + 1).
+  // The tile loads and the end-of-step wait run at raised wavefront priority,
+  // so that they do not queue behind the other wavefront's arithmetic on the
+  // SIMD (measured: about 1.5% faster at N = 4096).
   auto step = [&](const __bf16* kn, const __bf16* vc, __bf16* kf, __bf16* vf, int it) {
+    __builtin_amdgcn_s_setprio(2);
     if (it + 2 < ntiles) fill.issue(kf, rk, w, (it + 2) * kBN);
     if (it + 1 < ntiles) fill.issue(vf, rv, w, (it + 1) * kBN);
+    __builtin_amdgcn_s_setprio(0);
     f32x16 sn[2];
     if (it < nt_w) {
       const int t0 = it * kBN;
@@ -317,8 +322,10 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
     sc[0] = sn[0];
     sc[1] = sn[1];
+    __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_s_waitcnt(0);   // this thread's loads for the next step have landed
     __syncthreads();                 // ... everyone's, and the stages read here are free again
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int it = 0; it < ntiles; it += 2) {
     step(k1s, v0s, k0s, v1s, it);
