@@ -362,12 +362,16 @@ void decode_wide_bf16(WideArgs a) {
     const int row = p / kCPR;
     fsrc[i] = row * kDK * 2 + wide_phys(row, p - row * kCPR) * 16;
   }
+  // The loads issue at raised wavefront priority, ahead of the score
+  // wavefront that shares the SIMD (2-5% shorter launches).
   auto fill = [&](__bf16* dst, int tile_idx) {
     const int t0 = min(t_begin + tile_idx * kTok, t_end);   // past the range: zeros
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + (wv * 64 + kFillThreads * i) * 8), 16,
                                                t0 * kDK * 2 + fsrc[i], 0, 0, kCacheDefault);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Step it: loads of tile it + 2, then tile it - 1 (weights in buffer
   // (it - 1) % 2), then wait for tile it + 1 and the step's barrier.
