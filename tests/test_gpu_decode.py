@@ -69,6 +69,10 @@ SMALL_CASES = [
     ("f32", 2, 8, 2, 64, [1, 300], 320, 64),
     ("f32", 2, 12, 3, 128, [129, 64], 192, 128),
     ("f32", 1, 20, 1, 64, [100], 128, 0),               # fp32, 20 heads on one (two head blocks)
+    # many segments per unit: the merge takes several rounds of eight rows per thread
+    ("bf16", 1, 8, 2, 64, [5000], 5120, 32),            # 157 segments, 128 per round at d = 64
+    ("bf16", 1, 8, 2, 128, [4500], 4608, 32),           # 141 segments, 64 per round at d = 128
+    ("f32", 1, 4, 1, 64, [3000], 3072, 32),             # 94 segments
 ]
 
 
