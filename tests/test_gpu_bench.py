@@ -1,0 +1,55 @@
+"""bench.py end to end on the GPU: one short default run prints one JSON line
+with every field of the reporting contract, the roofline and the CPU
+baseline, and values that are consistent with each other."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from gpu_util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args]
+    say("running", " ".join(cmd[2:]))
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=180, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+def test_default_bench_line():
+    need_gpu()
+    d = run_bench("--steps", "4", "--warmup", "1", "--cpu-budget", "0.5")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 4 and d["warmup"] == 1
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["dtype"] == "bf16"
+    assert "workload" in d["config"]
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert 0 < rf["achieved"] < rf["peak"]
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], abs=1e-4)
+    # the step (split + merge) reads the same K/V as the split kernel alone, so it is not faster
+    assert d["value"] <= rf["achieved"] * 1.05
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    for part, bound in (("prefill", "mfma"), ("prefill_backward", "mfma")):
+        p = d[part]
+        assert p["value"] > 0 and p["roofline"]["bound"] == bound
+        assert 0 < p["roofline"]["frac"] < 1
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2 and "one GPU" in r.stderr
