@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
-    "gqa_decode_plan", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
+    "gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
     "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
     "gqa_decode_wide_plan", "gqa_decode_wide",
     "GQA_F32", "GQA_BF16",
@@ -70,6 +70,10 @@ def load_library():
     lib.gqa_abi_version.restype = I32
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_status_string.argtypes = [I32]
+    lib.gqa_status_str.restype = ctypes.c_char_p
+    lib.gqa_status_str.argtypes = [ctypes.c_int]
+    lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_decode_workspace_bytes.argtypes = [I32] * 4
     lib.gqa_last_hip_error.restype = ctypes.c_char_p
     lib.gqa_decode_plan.restype = I32
     lib.gqa_decode_plan.argtypes = [I32] * 7 + [ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -153,6 +157,12 @@ def gqa_decode_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: i
                                                   max_seq_len, dtype, split_tokens,
                                                   ctypes.byref(c), ctypes.byref(n), ctypes.byref(w)))
     return Plan(c.value, n.value, w.value)
+
+
+def gqa_decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_seq_len: int) -> int:
+    """Decode workspace bytes that serve every KV-head count dividing
+    ``num_q_heads`` with automatic ranges (0 for invalid arguments)."""
+    return int(load_library().gqa_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len))
 
 
 def _decode_args(q, k_cache, v_cache, seq_lens):

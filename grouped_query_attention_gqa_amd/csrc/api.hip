@@ -153,7 +153,18 @@ const char* gqa_status_string(int32_t status) {
   }
 }
 
+const char* gqa_status_str(gqa_status status) { return gqa_status_string((int32_t)status); }
+
 const char* gqa_last_hip_error(void) { return g_last_hip_error; }
+
+size_t gqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len) {
+  // one KV head per query head: the most units, hence the most slots
+  gqa::DecodeShape s;
+  if (make_plan(batch, num_q_heads, num_q_heads, head_dim, max_seq_len, GQA_BF16, 0, 1.f, &s) != GQA_OK)
+    return 0;
+  return (size_t)gqa::decode_workspace_layout(s).total;
+}
 
 int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_seq_len, int32_t dtype,

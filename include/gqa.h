@@ -68,8 +68,11 @@ typedef enum gqa_dtype {
 /* Version of this ABI (GQA_ABI_VERSION). */
 int32_t gqa_abi_version(void);
 
-/* Static, NUL-terminated name of a status code ("GQA_OK", ...). */
+/* Static, NUL-terminated name of a status code ("GQA_OK", ...); an unknown
+ * code gives "GQA_ERR_UNKNOWN".  gqa_status_str is the same function under
+ * the short name. */
 const char* gqa_status_string(int32_t status);
+const char* gqa_status_str(gqa_status status);
 
 /* Text of the last HIP error seen by a call on this thread ("" if none). */
 const char* gqa_last_hip_error(void);
@@ -95,6 +98,19 @@ int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
                         int32_t head_dim, int32_t max_seq_len, int32_t dtype,
                         int32_t split_tokens, int32_t* range_tokens_out,
                         int32_t* workgroups_out, int64_t* workspace_bytes_out);
+
+/*
+ * Workspace bytes that cover gqa_decode (and its two stages) for every
+ * number of KV heads that divides num_q_heads, every dtype and automatic
+ * ranges (split_tokens = 0), given only the batch, the query heads, the head
+ * dimension and the cache capacity.  It is the size gqa_decode_plan reports
+ * for the shape with the most units (num_kv_heads = num_q_heads), which
+ * bounds every other grouping because a decode unit never covers fewer than
+ * one query head.  Returns 0 when the arguments are invalid (a size below 1,
+ * head_dim not 64 or 128, or a size overflow).  Pure host arithmetic.
+ */
+size_t gqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len);
 
 /*
  * One decode step of GQA over a KV cache: every query head of every sequence

@@ -36,6 +36,56 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+# Every entry point of include/gqa.h.  The first group are the calls of the
+# boundary as first specified (decode with a caller-sized workspace, causal
+# prefill, the version and the status text); every other export is listed with
+# the reason it exists, so a new export has to be added here knowingly.
+BOUNDARY_CALLS = {"gqa_decode", "gqa_decode_workspace_bytes", "gqa_prefill_causal", "gqa_abi_version",
+                  "gqa_status_str"}
+EXTRA_CALLS = {
+    "gqa_status_string": "status text taking the int32 the calls return (gqa_status_str takes the enum)",
+    "gqa_last_hip_error": "text of the HIP error behind GQA_ERR_HIP",
+    "gqa_decode_plan": "exact workspace for one (Hkv, dtype, range size), the grid and the range size",
+    "gqa_decode_split": "first decode stage alone (partials), the cut a sequence-parallel decode merges across",
+    "gqa_decode_merge": "second decode stage alone (log-sum-exp merge of the partials)",
+    "gqa_decode_paged": "decode over a paged cache (block table)",
+    "gqa_decode_paged_split": "first stage of the paged decode",
+    "gqa_decode_fp8": "decode over an E4M3 cache with per-KV-head scales",
+    "gqa_decode_fp8_split": "first stage of the E4M3 decode",
+    "gqa_decode_wide_plan": "workspace and ranges of the wide-row decode",
+    "gqa_decode_wide": "decode over 576-column rows that are key and value (absorbed-MLA shape)",
+    "gqa_prefill_backward_workspace": "workspace of the prefill backward",
+    "gqa_prefill_causal_backward": "gradients of causal prefill",
+}
+
+
+def test_exports_match_the_boundary_table(lib):
+    names = set(declared_functions())
+    assert BOUNDARY_CALLS <= names
+    assert names == BOUNDARY_CALLS | set(EXTRA_CALLS), sorted(names ^ (BOUNDARY_CALLS | set(EXTRA_CALLS)))
+
+
+def test_status_str_matches_status_string(lib):
+    for code in range(-1, 9):
+        assert lib.gqa_status_str(code) == lib.gqa_status_string(code)
+
+
+def test_workspace_bytes_cover_every_grouping():
+    for (B, hq, d, tcap) in [(32, 32, 128, 8192), (64, 32, 128, 32768), (4, 16, 128, 131072),
+                             (1, 8, 64, 256), (3, 71, 128, 320), (2, 12, 64, 1)]:
+        bound = gqa.gqa_decode_workspace_bytes(B, hq, d, tcap)
+        assert bound > 0
+        for hkv in [h for h in range(1, hq + 1) if hq % h == 0]:
+            for dt in (F32, BF16, 2):
+                assert gqa.gqa_decode_plan(B, hq, hkv, d, tcap, dt).workspace_bytes <= bound, (B, hq, hkv, d)
+        assert gqa.gqa_decode_plan(B, hq, hq, d, tcap, BF16).workspace_bytes == bound
+
+
+@pytest.mark.parametrize("args", [(0, 8, 64, 256), (1, 0, 64, 256), (1, 8, 96, 256), (1, 8, 64, 0)])
+def test_workspace_bytes_zero_for_bad_arguments(args):
+    assert gqa.gqa_decode_workspace_bytes(*args) == 0
+
+
 def test_version_and_status_strings(lib):
     assert lib.gqa_abi_version() == 1
     for code, name in [(OK, b"GQA_OK"), (NULL, b"GQA_ERR_NULL"), (SHAPE, b"GQA_ERR_SHAPE"),

@@ -60,6 +60,8 @@ SMALL = [
     (1, 8, 2, 515, 128),     # five key workgroups, ragged last
     (2, 4, 1, 640, 64),      # MQA-style group 4, d = 64, several key workgroups
     (1, 3, 3, 389, 128),     # MHA, 128 positions per dq tile
+    (1, 32, 8, 300, 128),    # 8 units: the per-XCD grouping of the prefill-4k launch
+    (2, 16, 8, 200, 64),     # 16 units, d = 64
 ]
 
 

@@ -62,20 +62,20 @@ def test_fp8_small_full_parity(case):
     assert err <= TOL["bf16"]
 
 
-def test_fp8_llama3_8b_full_size_sampled():
+def test_fp8_llama3_8b_full_size():
+    """All 32 x 32 output rows of the llama3-8b workload over its E4M3 cache,
+    one sequence per oracle call."""
     need_gpu()
     cfg = gi.CONFIGS["llama3-8b"]
     fp = gi.make_fp8(gi.make_decode(cfg))
     say("fp8", gi.describe(cfg))
     got = run_fp8(fp)
-    assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(7)
     worst = 0.0
-    for b in [0, 31] + rng.integers(0, 32, 4).tolist():
+    for b in range(cfg.batch):
         ref = oracle.decode_fp8(gi.to_f64(fp.q[b:b + 1], "bf16"), fp.k_cache[b:b + 1], fp.v_cache[b:b + 1],
                                 fp.k_scale, fp.v_scale, fp.seq_lens[b:b + 1], cfg.scale)
         worst = max(worst, max_err(got[b:b + 1], ref))
-    say("fp8 llama3-8b sampled max err", worst)
+    say("fp8 llama3-8b max err", worst)
     assert worst <= TOL["bf16"]
 
 
