@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
-    "gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
+    "gqa_decode_plan", "gqa_decode_workspace_bytes", "decode_workspace", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
     "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
     "gqa_decode_wide_plan", "gqa_decode_wide",
     "GQA_F32", "GQA_BF16",
@@ -178,9 +178,15 @@ def _decode_args(q, k_cache, v_cache, seq_lens):
     return dev, B, Hq, Hkv, tcap, d, _dtype_code(q)
 
 
+def decode_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device workspace of ``nbytes`` for the decode entry points (its
+    contents on entry do not matter)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def _workspace(workspace, plan: Plan, dev):
     if workspace is None:
-        return torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+        return decode_workspace(plan.workspace_bytes, dev)
     _require(workspace.is_cuda and workspace.device == dev and workspace.is_contiguous(),
              "workspace must be a contiguous tensor on the same device")
     return workspace

@@ -51,7 +51,6 @@ constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kBN = tiles::kRows;   // keys per tile
 constexpr int kXcds = 8;
 constexpr int kPrefillThreads = tiles::kThreads;
-constexpr float kSlack = 8.f;   // log2 of the largest weight before a rescale
 
 // Per-lane constants of a wavefront: its Q operands and the LDS element
 // offsets of its K and V operands within a tile.  The tile swizzle repeats
@@ -67,10 +66,11 @@ struct Lane {
   int v_dx[DB];        // offset correction of the same column 8 keys later
 };
 
-// Online-softmax state of a wavefront's 32 query rows.
+// Online-softmax state of a wavefront's 32 query rows: weights are
+// 2^(s * scale * log2 e - r) for a per-row reference point r (log2 domain).
 template <int D>
 struct RowState {
-  float m, lsum;              // reference point (log2 domain) and this lane's share of the sum
+  float r, lsum;              // reference point and this lane's share of the sum
   f32x16 acc[D / 32];         // O^T[d, rows]
 };
 
@@ -101,33 +101,30 @@ __device__ __forceinline__ void mask_scores(f32x16 (&sc)[2], int t0, int pos, in
 }
 
 // One pipelined step's arithmetic in one branch-free block: the scores of
-// the next tile (K reads and MFMAs into sn) and the weights of this one (sc
-// -> bf16 P^T as four B operands: key chunk c holds keys 16c + 4j + 0..3,
-// then 16c + 8 + 4j + 0..3).  It is written as KSTEPS groups fenced by
-// scheduling barriers: group kk issues the K reads of step kk + 1, the two
-// MFMAs of step kk and a slice of the weights' arithmetic, so the weights
-// are computed while the matrix core runs and the register footprint stays
-// that of one step.  The reference point st.m moves only when a row's tile
-// maximum exceeds it by more than kSlack; the accumulators' rescale by
-// alpha, when that happened in some row (any_grow), is left to the caller.
-// mult > 0 multiplies the raw scores into the log2 domain (scale * log2 e,
-// folded into one FMA per weight, so a positive factor keeps the maximum
-// the maximum); the caller passes scores already scaled and mult = 1 for a
-// zero or negative scale.
+// the next tile (K reads and MFMAs into sn) and the weights of this one
+// (2^(sc * mult - r) -> bf16 P^T as four B operands: key chunk c holds keys
+// 16c + 4j + 0..3, then 16c + 8 + 4j + 0..3) with this lane's share of
+// their sum.  It is written as KSTEPS groups fenced by scheduling barriers:
+// group kk issues the K reads of step kk + 1, the two MFMAs of step kk and
+// four of the weights, so the weights are computed while the matrix core
+// runs.  No row maximum is taken here: the weights are relative to the
+// reference point, and the caller checks afterwards that none of them grew
+// past 2^8.  mult > 0 multiplies raw scores into the log2 domain (scale *
+// log2 e, folded into the weight's FMA); the caller passes scores already
+// scaled and mult = 1 for a zero or negative scale.
 template <int D>
 __device__ __forceinline__ void scores_and_weights(const __bf16* kn, const Lane<D>& ln, f32x16 (&sn)[2],
-                                                   const f32x16 (&sc)[2], RowState<D>& st, bf16x8 (&pb)[4],
-                                                   float& alpha, bool& any_grow, float mult) {
+                                                   const f32x16 (&sc)[2], float mult, float r, bf16x8 (&pb)[4],
+                                                   float& ps) {
   constexpr int KSTEPS = Lane<D>::KSTEPS;
-  constexpr int kPerGroup = (32 + KSTEPS - 3) / (KSTEPS - 2);   // weights per group after the two max groups
+  constexpr int kPerGroup = 32 / KSTEPS;   // weights per group
   static_assert(kPerGroup % 2 == 0, "weights pair up for the row sums");
   sn[0] = f32x16{};
   sn[1] = f32x16{};
   bf16x8 kop[2][2];
   kop[0][0] = load_bf16x8(kn + ln.k_rd[0]);
   kop[0][1] = load_bf16x8(kn + ln.k_rd[0] + 32 * D);
-  float mx = -INFINITY, m_new = 0.f;
-  float ps = 0.f;
+  ps = 0.f;
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -137,39 +134,58 @@ __device__ __forceinline__ void scores_and_weights(const __bf16* kn, const Lane<
     }
     sn[0] = mfma32(kop[kk & 1][0], ln.qb[kk], sn[0]);
     sn[1] = mfma32(kop[kk & 1][1], ln.qb[kk], sn[1]);
-    if (kk < 2) {
-      // the row maximum: key block kk
+    // weights e0 .. e0 + kPerGroup - 1 of the 32 (element e: block e / 16, register e % 16)
+    const int e0 = kk * kPerGroup;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
-      if (kk == 1) {
-        // rows pair lanes l and l + 32: swap halves on the VALU instead of a shuffle through LDS
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * mult;
-        // every row's first tile holds key 0, so st.m is finite from then on
-        const bool grow = mx > st.m + kSlack;
-        m_new = grow ? mx : st.m;
-        alpha = fast_exp2(st.m - m_new);
-        any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
-        st.m = m_new;
-      }
-    } else {
-      // weights e0 .. e0 + kPerGroup - 1 of the 32 (element e: block e / 16, register e % 16)
-      const int e0 = (kk - 2) * kPerGroup;
-#pragma unroll
-      for (int e = e0; e < e0 + kPerGroup && e < 32; ++e) {
-        float pe = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], mult, -m_new));
-        asm volatile("" : "+v"(pe));   // keeps the weight in this group (not sunk to its use)
-        pb[e >> 3][e & 7] = (__bf16)pe;
-      }
-      // the denominator sums exactly the bf16 weights PV uses (2 per dot)
-#pragma unroll
-      for (int e = e0; e < e0 + kPerGroup && e < 32; e += 2)
-        ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]}, ones, ps, false);
-      asm volatile("" : "+v"(ps));
+    for (int e = e0; e < e0 + kPerGroup; ++e) {
+      float pe = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], mult, -r));
+      asm volatile("" : "+v"(pe));   // keeps the weight in this group (not sunk to its use)
+      pb[e >> 3][e & 7] = (__bf16)pe;
     }
+    // the denominator sums exactly the bf16 weights PV uses (2 per dot)
+#pragma unroll
+    for (int e = e0; e < e0 + kPerGroup; e += 2)
+      ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]}, ones, ps, false);
+    asm volatile("" : "+v"(ps));
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.lsum = st.lsum * alpha + ps;
+}
+
+// The rare path of a step, taken when some weight of the tile may exceed
+// 2^8 (a lane's partial sum above 2^8, which includes overflow to infinity)
+// or on a wavefront's first tile (forced: r then becomes the first tile's
+// row maximum).  A row whose tile maximum exceeds r + 8 moves its reference
+// point up to that maximum: its weights are recomputed and its accumulators
+// and sum so far are rescaled by 2^(r_old - r_new).
+template <int D>
+__device__ __forceinline__ void rebase_rows(RowState<D>& st, const f32x16 (&sc)[2], float mult, bf16x8 (&pb)[4],
+                                            float& ps, bool first) {
+  constexpr float kSlack = 8.f;   // log2 of the largest weight kept without a rebase
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+  // rows pair lanes l and l + 32; a positive mult keeps the maximum the maximum
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * mult;
+  // every row's first tile holds key 0, so mx is finite there
+  const float r_new = (first || mx > st.r + kSlack) ? mx : st.r;
+  if (__builtin_amdgcn_ballot_w64(r_new != st.r) == 0) return;   // the weights stand
+  if (!first) {   // (on the first tile the sum and accumulators are still zero)
+    const float alpha = fast_exp2(st.r - r_new);
+    st.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.acc[i] *= alpha;
+  }
+  st.r = r_new;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) pb[e >> 3][e & 7] = (__bf16)fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], mult, -r_new));
+#pragma unroll
+  for (int e = 0; e < 32; e += 2)
+    ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]}, ones, ps, false);
 }
 
 // O^T[d, rows] += V^T[d, 16 keys] P^T[16 keys, rows] over the tile's four
@@ -232,7 +248,7 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS addresses stay scalar
   const int row = lane & 31;   // query row within the wave (B/D column)
   const int j = lane >> 5;     // contraction group
   const int head = kvh * g + hb * gw + (32 * w) / mq;
@@ -263,7 +279,7 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   const tiles::TileFill<D> fill(tid);
 
   RowState<D> st;
-  st.m = -INFINITY;
+  st.r = 0.f;
   st.lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < DB; ++i) st.acc[i] = f32x16{};
@@ -291,7 +307,7 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
   // One step; kn/vc hold K(it + 1)/V(it), kf/vf receive K(it + 2)/V(it + 1).
   // The tile loads and the end-of-step wait run at raised wavefront priority,
   // so that they do not queue behind the other wavefront's arithmetic on the
-  // SIMD (measured: about 1.5% faster at N = 4096).
+  // SIMD.
   auto step = [&](const __bf16* kn, const __bf16* vc, __bf16* kf, __bf16* vf, int it) {
     __builtin_amdgcn_s_setprio(2);
     if (it + 2 < ntiles) fill.issue(kf, rk, w, (it + 2) * kBN);
@@ -308,16 +324,14 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
           for (int r = 0; r < 16; ++r) sc[kb][r] = sc[kb][r] == -INFINITY ? -INFINITY : sc[kb][r] * scale_log2;
       }
+      const float mult = scale_log2 > 0.f ? scale_log2 : 1.f;
       // (after the wavefront's last tile the scores of the next are computed
       // but never used: reading a stage that holds no tile is harmless)
       bf16x8 pb[4];
-      float alpha;
-      bool any_grow;
-      scores_and_weights<D>(kn, ln, sn, sc, st, pb, alpha, any_grow, scale_log2 > 0.f ? scale_log2 : 1.f);
-      if (any_grow) {
-#pragma unroll
-        for (int i = 0; i < DB; ++i) st.acc[i] *= alpha;
-      }
+      float ps;
+      scores_and_weights<D>(kn, ln, sn, sc, mult, st.r, pb, ps);
+      if (__builtin_amdgcn_ballot_w64(it == 0 || !(ps <= 256.f)) != 0) rebase_rows<D>(st, sc, mult, pb, ps, it == 0);
+      st.lsum += ps;
       accumulate<D>(vc, ln, pb, st);
     }
     sc[0] = sn[0];
@@ -346,7 +360,7 @@ void prefill_causal_bf16(const __bf16* __restrict__ q, const __bf16* __restrict_
         for (int r = 0; r < 4; ++r) o4[r] = st.acc[db][4 * r4 + r] * inv;
         *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * j) = o4;
       }
-    if (lse != nullptr && j == 0) lse[((size_t)b * hq + head) * n + pos] = (st.m + __log2f(lsum)) * kLn2;
+    if (lse != nullptr && j == 0) lse[((size_t)b * hq + head) * n + pos] = (st.r + __log2f(lsum)) * kLn2;
   }
 }
 

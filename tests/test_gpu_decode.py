@@ -13,15 +13,28 @@ from gpu_util import TOL, decode_tensors, dev, max_err, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(inp, split_tokens=0, poison_workspace=True):
+def run_decode(inp, split_tokens=0, stages=False):
+    """One decode call through the C ABI.
+
+    stages=False: gqa_decode on a workspace that a call on other queries
+    has just used, so it holds that call's partials (stale values that a
+    read of an unwritten slot would pick up).
+    stages=True: gqa_decode_split then gqa_decode_merge on a workspace filled
+    with 0xFF bytes (NaN in every float slot), so unwritten partials show."""
     q, k, v, lens = decode_tensors(inp)
     B, Hq, d = q.shape
-    plan = gqa.gqa_decode_plan(B, Hq, k.shape[1], d, k.shape[2],
-                               gqa.GQA_BF16 if inp.cfg.dtype == "bf16" else gqa.GQA_F32, split_tokens)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
-    if poison_workspace:
-        ws.fill_(0xFF)   # NaN in every float slot: unwritten partials would show
-    out = gqa.gqa_decode(q, k, v, lens, scale=inp.cfg.scale, workspace=ws, split_tokens=split_tokens)
+    Hkv, tcap = k.shape[1], k.shape[2]
+    dt = gqa.GQA_BF16 if inp.cfg.dtype == "bf16" else gqa.GQA_F32
+    plan = gqa.gqa_decode_plan(B, Hq, Hkv, d, tcap, dt, split_tokens)
+    ws = gqa.decode_workspace(plan.workspace_bytes)
+    if stages:
+        ws.fill_(0xFF)
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+        gqa.gqa_decode_split(q, k, v, lens, out, ws, scale=inp.cfg.scale, split_tokens=split_tokens)
+        gqa.gqa_decode_merge(lens, out, ws, Hkv, tcap, dt, split_tokens)
+    else:
+        gqa.gqa_decode(-q, k, v, lens, scale=inp.cfg.scale, workspace=ws, split_tokens=split_tokens)
+        out = gqa.gqa_decode(q, k, v, lens, scale=inp.cfg.scale, workspace=ws, split_tokens=split_tokens)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -62,13 +75,14 @@ SMALL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("stages", [False, True], ids=["one-call", "two-stage"])
 @pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}on{c[3]}-d{c[4]}-split{c[7]}")
-def test_small_shapes_full_parity(case):
+def test_small_shapes_full_parity(case, stages):
     need_gpu()
     dt, B, Hq, Hkv, d, lens, tcap, split = case
     inp = gi.small_decode(dt, B, Hq, Hkv, d, lens, tcap, seed=zlib.crc32(repr(case).encode()) % 100000)
-    say("small", case)
-    got = run_decode(inp, split)
+    say("small", case, "two-stage" if stages else "one-call")
+    got = run_decode(inp, split, stages)
     ref = oracle_full(inp)
     err = max_err(got, ref)
     say("max err", err)

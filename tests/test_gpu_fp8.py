@@ -26,8 +26,9 @@ def run_fp8(fp, split_tokens=0, v_scale=None):
         vs = torch.from_numpy(v_scale).cuda()
     B, Hq, d = q.shape
     plan = gqa.gqa_decode_plan(B, Hq, k.shape[1], d, k.shape[2], gqa.GQA_FP8_E4M3, split_tokens)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
-    ws.fill_(0xFF)
+    ws = gqa.decode_workspace(plan.workspace_bytes)
+    # a call on other queries first: the workspace then holds stale partials
+    gqa.gqa_decode_fp8(-q, k, v, ks, vs, lens, scale=fp.cfg.scale, workspace=ws, split_tokens=split_tokens)
     out = gqa.gqa_decode_fp8(q, k, v, ks, vs, lens, scale=fp.cfg.scale, workspace=ws, split_tokens=split_tokens)
     torch.cuda.synchronize()
     return out.cpu().numpy()
@@ -60,6 +61,24 @@ def test_fp8_small_full_parity(case):
     err = max_err(got, fp8_oracle(fp))
     say("max err", err)
     assert err <= TOL["bf16"]
+
+
+def test_fp8_two_stage_matches_oracle():
+    """gqa_decode_fp8_split + gqa_decode_merge on a workspace of 0xFF bytes
+    (NaN in every float slot, so unwritten partials would show)."""
+    need_gpu()
+    inp = gi.small_decode("bf16", 3, 32, 2, 128, [2000, 1, 513], 2048, seed=97)
+    fp = gi.make_fp8(inp)
+    q, k, v, ks, vs, lens = tensors(fp)
+    for split in (0, 64):
+        plan = gqa.gqa_decode_plan(3, 32, 2, 128, 2048, gqa.GQA_FP8_E4M3, split)
+        ws = gqa.decode_workspace(plan.workspace_bytes)
+        ws.fill_(0xFF)
+        out = gqa.gqa_decode_fp8(q, k, v, ks, vs, lens, scale=fp.cfg.scale, workspace=ws, split_tokens=split,
+                                 stage="split")
+        gqa.gqa_decode_merge(lens, out, ws, 2, 2048, gqa.GQA_FP8_E4M3, split)
+        torch.cuda.synchronize()
+        assert max_err(out.cpu().numpy(), fp8_oracle(fp)) <= TOL["bf16"], split
 
 
 def test_fp8_llama3_8b_full_size():

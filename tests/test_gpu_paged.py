@@ -21,8 +21,9 @@ def run_paged(pg, split_tokens=0, table=None):
     lens = torch.from_numpy(pg.seq_lens).cuda()
     B, Hq, d = q.shape
     plan = gqa.gqa_decode_plan(B, Hq, kp.shape[1], d, bt.shape[1] * pg.page_size, gqa.GQA_BF16, split_tokens)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
-    ws.fill_(0xFF)   # NaN in every float slot: unwritten partials would show
+    ws = gqa.decode_workspace(plan.workspace_bytes)
+    # a call on other queries first: the workspace then holds stale partials
+    gqa.gqa_decode_paged(-q, kp, vp, bt, lens, scale=pg.cfg.scale, workspace=ws, split_tokens=split_tokens)
     out = gqa.gqa_decode_paged(q, kp, vp, bt, lens, scale=pg.cfg.scale, workspace=ws,
                                split_tokens=split_tokens)
     torch.cuda.synchronize()
@@ -77,6 +78,27 @@ def test_paged_forced_splits_match_contiguous():
         got = run_paged(pg, split_tokens=split)
         assert max_err(got, paged_oracle(pg)) <= TOL["bf16"], split
         assert np.array_equal(got, run_contiguous(inp, split_tokens=split)), split
+
+
+def test_paged_two_stage_matches_oracle():
+    """gqa_decode_paged_split + gqa_decode_merge on a workspace of 0xFF bytes
+    (NaN in every float slot, so unwritten partials would show)."""
+    need_gpu()
+    inp = gi.small_decode("bf16", 3, 16, 2, 128, [3000, 1, 700], 3072, seed=93)
+    pg = gi.make_paged(inp, page_size=16, seed=8)
+    q = dev(pg.q, "bf16")
+    kp, vp = dev(pg.k_pages, "bf16"), dev(pg.v_pages, "bf16")
+    bt, lens = torch.from_numpy(pg.block_table).cuda(), torch.from_numpy(pg.seq_lens).cuda()
+    tcap = bt.shape[1] * pg.page_size
+    for split in (0, 64):
+        plan = gqa.gqa_decode_plan(3, 16, 2, 128, tcap, gqa.GQA_BF16, split)
+        ws = gqa.decode_workspace(plan.workspace_bytes)
+        ws.fill_(0xFF)
+        out = gqa.gqa_decode_paged(q, kp, vp, bt, lens, scale=pg.cfg.scale, workspace=ws, split_tokens=split,
+                                   stage="split")
+        gqa.gqa_decode_merge(lens, out, ws, 2, tcap, gqa.GQA_BF16, split)
+        torch.cuda.synchronize()
+        assert max_err(out.cpu().numpy(), paged_oracle(pg)) <= TOL["bf16"], split
 
 
 def test_paged_llama3_8b_full_size():
