@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
-    "gqa_decode_plan", "gqa_decode_workspace_bytes", "decode_workspace", "gqa_decode", "gqa_decode_split", "gqa_decode_merge",
+    "gqa_decode_plan", "gqa_decode_workspace_bytes", "decode_workspace", "gqa_decode", "gqa_decode_noalloc", "gqa_decode_split",
+    "gqa_decode_merge",
     "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
     "gqa_decode_wide_plan", "gqa_decode_wide",
     "GQA_F32", "GQA_BF16",
@@ -80,6 +81,8 @@ def load_library():
                                                 ctypes.POINTER(I64)]
     lib.gqa_decode.restype = I32
     lib.gqa_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
+    lib.gqa_decode_noalloc.restype = I32
+    lib.gqa_decode_noalloc.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P]
     lib.gqa_decode_split.restype = I32
     lib.gqa_decode_split.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, I32, P, I64, P]
     lib.gqa_decode_merge.restype = I32
@@ -209,6 +212,22 @@ def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check("gqa_decode", lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                         _ptr(out), B, Hq, Hkv, d, tcap, scale, dt, split_tokens,
                                         _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def gqa_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       seq_lens: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None,
+                       split_tokens: int = 0) -> torch.Tensor:
+    """gqa_decode with the library's own per-GPU scratch instead of a
+    workspace: the C call allocates nothing (``out`` is the caller's)."""
+    dev, B, Hq, Hkv, tcap, d, dt = _decode_args(q, k_cache, v_cache, seq_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _require(out.dtype == torch.float32 and out.shape == (B, Hq, d), "out must be float32 [B,Hq,d]")
+    _on_gpu(q, out)
+    lib = load_library()
+    _check("gqa_decode_noalloc", lib.gqa_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, tcap, scale, dt,
+        split_tokens, _stream(dev)))
     return out
 
 

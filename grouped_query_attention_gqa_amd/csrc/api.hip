@@ -5,6 +5,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "gqa.h"
@@ -134,6 +137,43 @@ int32_t make_wide_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d_k, int3
   return GQA_OK;
 }
 
+// Scratch of gqa_decode_noalloc: device memory that exists from the moment
+// the code object is loaded on a GPU until the process ends, one copy per
+// GPU, so that the entry point never allocates.  Host code never passes the
+// array's name to a kernel (on the host it only names the symbol): it uses
+// the device address that hipGetSymbolAddress returns for the current GPU.
+constexpr int64_t kNoAllocScratchBytes = 16ll << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current GPU, looked up on the first
+// call on each GPU.  The decode kernels overwrite every scratch byte they
+// read (the split kernel writes the unit index and the partials that the
+// merge kernel reads), so nothing in it needs clearing.
+int32_t noalloc_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return GQA_ERR_UNSUPPORTED;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      p = static_cast<char*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,6 +287,28 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (st != GQA_OK) return st;
   if (!aligned(out, 16)) return GQA_ERR_ALIGN;
   char* base = static_cast<char*>(workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, out, base, s, hs));
+  if (st != GQA_OK) return st;
+  return hip_status(gqa::launch_decode_merge(seq_lens, out, base, s, hs));
+}
+
+int32_t gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, float* out, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len, float scale,
+                           int32_t dtype, int32_t split_tokens, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return GQA_ERR_NULL;
+  if (dtype == GQA_FP8_E4M3) return GQA_ERR_UNSUPPORTED;   // needs the scales: gqa_decode_fp8
+  gqa::DecodeShape s;
+  int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, dtype, split_tokens, scale, &s);
+  if (st != GQA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4))
+    return GQA_ERR_ALIGN;
+  if (gqa::decode_workspace_layout(s).total > kNoAllocScratchBytes) return GQA_ERR_WORKSPACE;
+  char* base = nullptr;
+  st = noalloc_scratch(&base);
+  if (st != GQA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   st = hip_status(gqa::launch_decode_split(q, k_cache, v_cache, seq_lens, out, base, s, hs));
   if (st != GQA_OK) return st;

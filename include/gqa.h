@@ -140,6 +140,24 @@ int32_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                    void* stream);
 
 /*
+ * gqa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments, result and errors as gqa_decode, minus the workspace: the
+ * library keeps a device scratch array of 16 MiB per GPU (it exists from
+ * the library's load until the process ends) and this call neither
+ * allocates nor frees anything.  A shape whose workspace (gqa_decode_plan)
+ * exceeds 16 MiB gets GQA_ERR_WORKSPACE; fp32 and bf16 only.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or threads without ordering) race and must be
+ * serialised by the caller.
+ */
+int32_t gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, float* out, int32_t batch,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_seq_len, float scale, int32_t dtype,
+                           int32_t split_tokens, void* stream);
+
+/*
  * First stage of gqa_decode (the kernel that reads the KV cache).  Rows of
  * out whose sequence falls in a single range are written in final form;
  * every other (sequence, query head) leaves one normalised partial output

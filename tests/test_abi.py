@@ -46,6 +46,7 @@ EXTRA_CALLS = {
     "gqa_status_string": "status text taking the int32 the calls return (gqa_status_str takes the enum)",
     "gqa_last_hip_error": "text of the HIP error behind GQA_ERR_HIP",
     "gqa_decode_plan": "exact workspace for one (Hkv, dtype, range size), the grid and the range size",
+    "gqa_decode_noalloc": "gqa_decode for callers that cannot allocate (library-owned per-GPU scratch)",
     "gqa_decode_split": "first decode stage alone (partials), the cut a sequence-parallel decode merges across",
     "gqa_decode_merge": "second decode stage alone (log-sum-exp merge of the partials)",
     "gqa_decode_paged": "decode over a paged cache (block table)",
@@ -144,6 +145,25 @@ def test_decode_validation(lib):
     assert _decode(lib, ws_bytes=16) == WS
     need = gqa.gqa_decode_plan(1, 8, 2, 64, 256, BF16).workspace_bytes
     assert _decode(lib, ws_bytes=need - 1) == WS
+
+
+def _noalloc(lib, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=1, hq=8, hkv=2, d=64, tcap=256, dtype=BF16,
+             split=0):
+    return lib.gqa_decode_noalloc(q, k, v, lens, out, B, hq, hkv, d, tcap, 0.125, dtype, split, None)
+
+
+def test_noalloc_validation(lib):
+    """Argument errors of the allocation-free decode, all before any HIP call."""
+    assert _noalloc(lib, q=None) == NULL
+    assert _noalloc(lib, out=None) == NULL
+    assert _noalloc(lib, hkv=3) == SHAPE
+    assert _noalloc(lib, d=96) == UNSUP
+    assert _noalloc(lib, dtype=2) == UNSUP             # E4M3 needs the scales of gqa_decode_fp8
+    assert _noalloc(lib, k=MISALIGNED) == ALIGN
+    # a shape whose workspace exceeds the library's 16 MiB scratch
+    big = gqa.gqa_decode_plan(4096, 64, 64, 128, 65536, BF16).workspace_bytes
+    assert big > 16 << 20
+    assert _noalloc(lib, B=4096, hq=64, hkv=64, d=128, tcap=65536) == WS
 
 
 def test_split_and_merge_validation(lib):

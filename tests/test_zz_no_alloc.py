@@ -1,0 +1,76 @@
+"""gqa_decode_noalloc (the decode entry point that allocates nothing and uses
+the library's per-GPU scratch) through the C ABI, against gqa_decode with a
+caller workspace (the same kernels) and against the float64 oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import grouped_query_attention_gqa_amd as gqa
+import oracle
+from gpu_util import TOL, decode_tensors, max_err, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def noalloc(inp, split_tokens=0):
+    """One call of the C entry point on the current stream; returns out."""
+    lib = gqa.load_library()
+    q, k, v, lens = decode_tensors(inp)
+    B, Hq, d = q.shape
+    Hkv, tcap = k.shape[1], k.shape[2]
+    dt = gqa.GQA_BF16 if inp.cfg.dtype == "bf16" else gqa.GQA_F32
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    st = lib.gqa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens.data_ptr(), out.data_ptr(), B, Hq,
+                                Hkv, d, tcap, ctypes.c_float(inp.cfg.scale), dt, split_tokens,
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, gqa.load_library().gqa_status_string(st)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def with_workspace(inp, split_tokens=0):
+    q, k, v, lens = decode_tensors(inp)
+    out = gqa.gqa_decode(q, k, v, lens, scale=inp.cfg.scale, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def reference(inp):
+    dt = inp.cfg.dtype
+    return oracle.decode(gi.to_f64(inp.q, dt), gi.to_f64(inp.k_cache, dt), gi.to_f64(inp.v_cache, dt),
+                         inp.seq_lens, inp.cfg.scale)
+
+
+CALLS = [
+    # dtype, B, Hq, Hkv, d, lens, T_cap, split: each call smaller than the one before
+    ("bf16", 8, 32, 8, 128, [8192, 5000, 1, 7777, 4096, 300, 8192, 2048], 8192, 0),
+    ("bf16", 3, 16, 2, 128, [1000, 37, 640], 1024, 0),
+    ("bf16", 2, 8, 2, 64, [700, 129], 704, 64),   # many ranges per sequence: two-level merge
+    ("f32", 1, 8, 2, 64, [256], 256, 64),          # fp32: split and merge kernels
+]
+
+
+def test_noalloc_matches_workspace_entry_on_successive_calls():
+    need_gpu()
+    for i, (dt, B, Hq, Hkv, d, lens, tcap, split) in enumerate(CALLS):
+        inp = gi.small_decode(dt, B, Hq, Hkv, d, lens, tcap, seed=4100 + i)
+        say("noalloc call", i, dt, B, Hq, Hkv, d, lens, tcap, split)
+        got = noalloc(inp, split)
+        want = with_workspace(inp, split)
+        assert np.array_equal(got, want), i          # the same kernels on the same ranges
+        err = max_err(got, reference(inp))
+        say("noalloc max err", err)
+        assert err <= TOL[dt]
+
+
+def test_noalloc_repeated_call_is_bitwise_stable():
+    """The scratch keeps the previous call's partials, and every call
+    overwrites what it reads, so calling again gives the same bits."""
+    need_gpu()
+    inp = gi.small_decode("bf16", 4, 16, 1, 128, [4096, 4000, 100, 3000], 4096, seed=4200)
+    a = noalloc(inp)
+    b = noalloc(inp)
+    assert np.array_equal(a, b)
