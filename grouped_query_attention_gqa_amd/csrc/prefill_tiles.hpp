@@ -4,8 +4,8 @@
 //
 // A tile holds 64 rows of D bf16 values (rows are keys, or query positions
 // in the backward key/value kernel), in 16-byte chunks, with the chunk index
-// XOR-ed by a one-bit rotation of the row index.  That single layout serves
-// both reads without bank conflicts:
+// XOR-ed by a permutation g of the row index (period 16 rows).  That single
+// layout serves both reads without bank conflicts:
 //   row reads   (ds_read_b128): an operand whose lane index l%32 is the row
 //               and whose k-group l/32 picks 8 consecutive columns;
 //   transposed  (two ds_read_b64_tr_b16): an operand whose lane index l%32
@@ -29,14 +29,28 @@ constexpr int kThreads = 256;   // threads of the workgroups that fill a tile
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Physical 16-byte chunk of logical chunk c in row r: c ^ rot(r), with rot
-// a one-bit left rotation of r within the chunk-index width (a bijection
-// that is linear under XOR).
+// Physical 16-byte chunk of logical chunk c in row r: c ^ g(r).  The LDS
+// serves 256 bytes per cycle (64 banks of 4 bytes): a row read (16 bytes
+// per lane) takes 16 lanes per cycle, which are 16 consecutive rows at one
+// logical chunk, and a transposed read (8 bytes per lane) takes 32 lanes,
+// which are 4 consecutive rows (aligned to 4) at 4 consecutive chunks
+// (aligned to 4).  Both are conflict-free when the 16 or 32 accesses land
+// on distinct bank groups:
+//   D = 128 (16 chunks, 256 B per row): g(r) swaps the two 2-bit fields of
+//     r mod 16.  It is a permutation of 0..15 (row reads), and its upper
+//     two bits, r mod 4, differ within every aligned quad of rows
+//     (transposed reads: 4 rows x 4 chunks give 16 distinct chunks).
+//   D = 64 (8 chunks, 128 B per row, two rows per 256 B): g(r) = 4 * (bit 1
+//     of r) + (bits 2..3 of r).  Rows of one parity get distinct g (row
+//     reads), and rows r, r + 2 of an aligned quad differ in g's upper bit
+//     (transposed reads).
+// (A one-bit rotation of r, used before, leaves the transposed reads with
+// two-way conflicts; the replacement was measured conflict-free with the
+// SQ_LDS_BANK_CONFLICT counter.)
 template <int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
-  constexpr int BITS = CPR == 16 ? 4 : 3;
-  const int x = r & (CPR - 1);
-  return c ^ (((x << 1) | (x >> (BITS - 1))) & (CPR - 1));
+  if (CPR == 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Global byte offsets (relative to the tile's first row) of the chunks that
