@@ -618,8 +618,9 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
 // Log-sum-exp merge of the segment partials: one workgroup per (query head,
 // sequence).  Threads hold 4 head coordinates each; D/4 threads cover one
 // partial row, so the 256 threads form 1024/D row groups.  A round loads
-// eight rows per thread, each row's lse and output together, so one round
-// trip to memory serves up to 8192/D segments.  Every row group keeps its
+// sixteen rows per thread, each row's lse and output together, so one round
+// trip to memory serves up to 16384/D segments (the 128 segments per unit of
+// a 131072-token MQA sequence in one round at d = 128).  Every row group keeps its
 // own running maximum (online softmax over the partials); the groups are
 // then combined through LDS against the largest.  Units written directly by
 // a single segment are skipped; empty sequences get zeros.
@@ -633,7 +634,7 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
                   float* __restrict__ out, int hq, int hkv, int g, int nhb, int tcap) {
   constexpr int C4 = D / 4;                  // float4 columns per row
   constexpr int ROWS = kMergeThreads / C4;   // row groups
-  constexpr int U = 8;                       // rows per thread per round
+  constexpr int U = 16;                      // rows per thread per round
   __shared__ f32x4 racc[ROWS][C4];
   __shared__ float rl[ROWS];
   __shared__ float rm[ROWS];
