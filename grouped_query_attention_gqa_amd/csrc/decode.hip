@@ -617,10 +617,9 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the segment partials: one workgroup per (query head,
 // sequence).  Threads hold 4 head coordinates each; D/4 threads cover one
-// partial row, so the 256 threads form 1024/D row groups.  A round loads
-// sixteen rows per thread, each row's lse and output together, so one round
-// trip to memory serves up to 16384/D segments (the 128 segments per unit of
-// a 131072-token MQA sequence in one round at d = 128).  Every row group keeps its
+// partial row, so the 256 threads form 1024/D row groups.  A round loads up
+// to eight rows per thread, each row's lse and output together, so one round
+// trip to memory serves up to 8192/D segments.  Every row group keeps its
 // own running maximum (online softmax over the partials); the groups are
 // then combined through LDS against the largest.  Units written directly by
 // a single segment are skipped; empty sequences get zeros.
@@ -634,7 +633,7 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
                   float* __restrict__ out, int hq, int hkv, int g, int nhb, int tcap) {
   constexpr int C4 = D / 4;                  // float4 columns per row
   constexpr int ROWS = kMergeThreads / C4;   // row groups
-  constexpr int U = 16;                      // rows per thread per round
+  constexpr int U = 8;                       // rows per thread per round
   __shared__ f32x4 racc[ROWS][C4];
   __shared__ float rl[ROWS];
   __shared__ float rm[ROWS];
@@ -655,8 +654,8 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
   if (ns <= 1) return;   // written directly by its only segment
 
   // Row group sr: segments sr, sr + ROWS, ...  Every segment holds at least
-  // one token, so its lse is finite; rows past ns are padding, loaded from
-  // the last segment and given lse -inf (weight 0).
+  // one token, so its lse is finite; rows past ns are padding with lse -inf
+  // (weight 0) and a zero output, and are not loaded.
   const int c4 = tid % C4;
   const int sr = tid / C4;
   float m = -INFINITY, L = 0.f;
@@ -667,9 +666,13 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * ROWS;
-      const size_t row = ((size_t)base + min(s, ns - 1)) * kDecodeHeadBlock + hl;
-      lr[u] = s < ns ? part_lse[row] : -INFINITY;
-      ov[u] = reinterpret_cast<const f32x4*>(part_o + row * D)[c4];
+      const size_t row = ((size_t)base + s) * kDecodeHeadBlock + hl;
+      lr[u] = -INFINITY;
+      ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < ns) {   // padding rows load nothing
+        lr[u] = part_lse[row];
+        ov[u] = reinterpret_cast<const f32x4*>(part_o + row * D)[c4];
+      }
     }
     float mn = m;
 #pragma unroll
