@@ -15,22 +15,27 @@
 // about equal, so the design is about keeping operand traffic through LDS
 // and the phases of a tile overlapped.  A workgroup is 8 wavefronts (two
 // per SIMD) serving a block of 64 query heads of one KV head over one token
-// range; the two blocks of a 128-head group run on the same XCD and share
+// range; the head blocks of a 128-head group run on the same XCD and share
 // the rows through L2.  32-token tiles of 576-column rows (36 KiB) go into a
-// ring of three LDS stages by direct global-to-LDS loads issued two tiles
-// ahead.  The wavefronts split into two roles that share each SIMD:
-//  * score wavefronts 0-3 take contraction columns 144 w .. +143 of S^T[32
-//    tok, 64 heads] (v_mfma_f32_32x32x16_bf16, Q^T in 72 registers, every K
-//    operand feeding both 32-head blocks), publish the partial scores to
-//    LDS, and issue the tile loads;
+// ring of four LDS stages by direct global-to-LDS loads, issued two tiles
+// ahead by the value wavefronts at raised wavefront priority.  The
+// wavefronts split into two roles that share each SIMD, each in its own
+// code path so their registers never overlap:
+//  * score wavefronts 0-3 own 16 heads each over all 576 columns: S^T[16
+//    tok, 16 heads] per half tile on v_mfma_f32_16x16x32_bf16 (Q^T as B
+//    operands in 72 registers, K operands read from LDS in groups of six,
+//    one group ahead of their MFMAs), then the weights of the tile's 32
+//    tokens, published as bf16 P[head][token] into one of two weight
+//    buffers;
 //  * value wavefronts 4-7 own output columns 128 (w - 4) .. +127 for all 64
-//    heads, O^T[128, 64] += V^T[128, 32 tok] P^T[32 tok, 64] (16 MFMAs per
-//    tile, 128 accumulation registers, no value column read twice), and sum
-//    the four partial scores of their 16 heads and weight them (bf16
-//    P[head][token] in LDS).
+//    heads: O^T[128, 64] += V^T[128, 32 tok] P^T[32 tok, 64] on
+//    v_mfma_f32_32x32x16_bf16 (16 MFMAs per tile, 128 accumulation
+//    registers, V^T through transposing LDS reads, no value column read
+//    twice), and they issue the tile loads.
 // In step it the score wavefronts work on tile it while the value
-// wavefronts accumulate tile it - 1, so the two kinds of MFMA work overlap
-// on every SIMD; two barriers per step.
+// wavefronts accumulate tile it - 1 from the other weight buffer, so the two
+// kinds of MFMA work overlap on every SIMD; with four tile stages and two
+// weight buffers one barrier per step suffices.
 // The weights of a range are taken against one fixed maximum per head, the
 // first tile's, so the accumulators never need a rescale.  Weights up to
 // 2^32 are harmless in bf16 and fp32 (sums stay far below the fp32 range

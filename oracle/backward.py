@@ -5,11 +5,11 @@ imports or calls this module.
 
 Source followed: study.greatitself.com, "Grouped-Query and Multi-Query
 Attention", section "Share keys and values without confusing query-head
-identity", its paragraph on training: a shared key or value tensor collects
-gradient from every query head of its group, and a reference may repeat K and
-V along the query-head axis and let differentiation sum the copies back onto
-the shared tensors.  That is exactly what this module does, with the chain
-rule written out per query head instead of left to an autodiff system.
+identity", its paragraph on training: each shared KV head receives the sum of
+the gradients of all query heads in its group.  The reference form the page
+allows expands K/V per query head and adds the per-head gradients back onto
+each shared KV head; this module does that, writing the chain rule out per
+query head instead of leaving it to an autodiff system.
 
 For one query head h with repeated K_h = K[h // g], V_h = V[h // g] and the
 loss gradient dO_h (the caller's upstream gradient of the output), the
