@@ -51,7 +51,11 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tca
   if ((int64_t)tcap * d * 4 > INT32_MAX) return GQA_ERR_SHAPE;
   const int64_t g = hq / hkv;
   const int64_t nhb = (g + gqa::kDecodeHeadBlock - 1) / gqa::kDecodeHeadBlock;
-  const int64_t units = (int64_t)batch * hkv * nhb;
+  // bf16 and E4M3 caches put two head blocks in one unit when the group has
+  // more than one block (one pass over the KV head for up to 32 heads)
+  const int hbu = (dtype != GQA_F32 && nhb > 1) ? 2 : 1;
+  const int64_t nhg = (nhb + hbu - 1) / hbu;
+  const int64_t units = (int64_t)batch * hkv * nhg;
   const int64_t work = units * (int64_t)tcap;   // upper bound on token-units
   int64_t ranges, grid;
   if (split_tokens == 0) {
@@ -63,8 +67,10 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tca
     grid = ranges < gqa::kPersistentWorkgroups ? ranges : gqa::kPersistentWorkgroups;
   }
   const int64_t slots = ranges + units;
-  if (units > INT32_MAX || slots > INT32_MAX / gqa::kDecodeHeadBlock) return GQA_ERR_SHAPE;
+  if (units > INT32_MAX || slots > INT32_MAX / (gqa::kDecodeHeadBlock * hbu)) return GQA_ERR_SHAPE;
   s->batch = batch;
+  s->hb = hbu;
+  s->nhg = (int)nhg;
   s->hq = hq;
   s->hkv = hkv;
   s->d = d;
@@ -199,11 +205,20 @@ const char* gqa_last_hip_error(void) { return g_last_hip_error; }
 
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len) {
-  // one KV head per query head: the most units, hence the most slots
-  gqa::DecodeShape s;
-  if (make_plan(batch, num_q_heads, num_q_heads, head_dim, max_seq_len, GQA_BF16, 0, 1.f, &s) != GQA_OK)
-    return 0;
-  return (size_t)gqa::decode_workspace_layout(s).total;
+  // the largest plan over the KV-head counts that divide num_q_heads (bf16
+  // plans bound fp32 and E4M3 ones: the same units or fewer, no wider rows)
+  int64_t most = 0;
+  for (int64_t a = 1; a * a <= num_q_heads; ++a) {
+    if (num_q_heads % a != 0) continue;
+    const int32_t hkvs[2] = {(int32_t)a, (int32_t)(num_q_heads / a)};
+    for (int32_t hkv : hkvs) {
+      gqa::DecodeShape s;
+      if (make_plan(batch, num_q_heads, hkv, head_dim, max_seq_len, GQA_BF16, 0, 1.f, &s) != GQA_OK) return 0;
+      const int64_t t = gqa::decode_workspace_layout(s).total;
+      if (t > most) most = t;
+    }
+  }
+  return (size_t)most;
 }
 
 int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

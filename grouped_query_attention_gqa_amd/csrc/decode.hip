@@ -308,14 +308,18 @@ __device__ __forceinline__ void load_tile_f8(DecodeTileF8<D>& t, __amdgpu_buffer
 
 // kPaged: K/V in a page pool addressed through a block table.  kFp8: K/V
 // stored as E4M3 codes with one float scale per KV head (k_scale folds into
-// the softmax scale, v_scale multiplies the normalised output).
-template <int D, bool kPaged, bool kFp8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA_DECODE_WAVES_PER_EU)))
+// the softmax scale, v_scale multiplies the normalised output).  HB: 16-head
+// blocks per unit; with HB = 2 a unit covers 32 query heads of one KV head,
+// both blocks scored from the same K registers and accumulated from the same
+// V tile, so a group of up to 32 heads reads its K/V once (two waves per
+// SIMD, as launched, leave a wavefront 256 registers for the second block).
+template <int D, bool kPaged, bool kFp8, int HB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HB == 1 ? GQA_DECODE_WAVES_PER_EU : 2)))
 void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kcv,
                        const void* __restrict__ vcv, const int32_t* __restrict__ lens,
                        float* __restrict__ out, float* __restrict__ part_o,
                        float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
-                       int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2,
+                       int hq, int hkv, int g, int nhg, int tcap, int q_fixed, float scale_log2,
                        PagedKV pk, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   static_assert(!(kPaged && kFp8), "paged FP8 caches are not supported");
   const __bf16* kc = static_cast<const __bf16*>(kcv);
@@ -332,7 +336,8 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
   __shared__ __align__(16) char smem[DecodeBf16Smem<D>::kBytes];
   __shared__ ScanSmem scan;
 
-  const int upb = hkv * nhb;
+  constexpr int UH = kDecodeHeadBlock * HB;   // query heads per unit (partial row width)
+  const int upb = hkv * nhg;
   const Stream st = stream_setup(scan, lens, batch, upb, tcap, q_fixed);
 
   const int lane = threadIdx.x & 63;
@@ -353,20 +358,23 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
     while (true) {
       const int t0 = (int)(lo - u.s);                      // first token of the segment
       const int nt = (int)(min(hi, u.s + u.t) - lo);       // tokens in the segment
-      const int kvh = u.j / nhb;
-      const int hb = u.j - kvh * nhb;
-      const int h_first = kvh * g + hb * kDecodeHeadBlock;
-      const int nh = min(kDecodeHeadBlock, g - hb * kDecodeHeadBlock);
+      const int kvh = u.j / nhg;
+      const int hg = u.j - kvh * nhg;
+      const int h_first = kvh * g + hg * UH;
+      const int nh_unit = min(UH, g - hg * UH);   // heads of this unit (at least one)
 
-      // Q^T as the B operand: lane holds q[h_first+n][8j + 32kk .. +7]
-      // (for an E4M3 cache: q[..][j*D/4 + 8kk .. +7], the K slot order).
-      bf16x8 qb[KSTEPS];
-      {
-        const __bf16* qrow = q + ((size_t)u.b * hq + h_first + min(n, nh - 1)) * D;
+      // Q^T as the B operand of block bk: lane holds q[h_first+16bk+n][8j + 32kk .. +7]
+      // (for an E4M3 cache: q[..][j*D/4 + 8kk .. +7], the K slot order);
+      // heads past the unit's last are zero.
+      bf16x8 qb[HB][KSTEPS];
+#pragma unroll
+      for (int bk = 0; bk < HB; ++bk) {
+        const int nh = nh_unit - kDecodeHeadBlock * bk;
+        const __bf16* qrow = q + ((size_t)u.b * hq + h_first + kDecodeHeadBlock * bk + max(0, min(n, nh - 1))) * D;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          qb[kk] = load_bf16x8(qrow + (kFp8 ? j * (D / 4) + 8 * kk : 8 * j + 32 * kk));
-          if (n >= nh) qb[kk] = bf16x8{};
+          qb[bk][kk] = nh > 0 ? load_bf16x8(qrow + (kFp8 ? j * (D / 4) + 8 * kk : 8 * j + 32 * kk)) : bf16x8{};
+          if (n >= nh) qb[bk][kk] = bf16x8{};
         }
       }
       const size_t seg_off = kPaged ? 0 : (((size_t)u.b * hkv + kvh) * (size_t)tcap + t0) * D * ELEM;
@@ -375,11 +383,16 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
       const float sl2 = kFp8 ? scale_log2 * k_scale[kvh] : scale_log2;
       const float vsc = kFp8 ? v_scale[kvh] : 1.f;
 
-      float m = -INFINITY;   // running max of head n (log2 domain), same in all 4 lane groups
-      float lsum = 0.f;      // this lane's share of the running denominator of head n
-      f32x4 acc[DBLK];
+      float m[HB];      // running max of head n of each block (log2 domain), same in all 4 lane groups
+      float lsum[HB];   // this lane's share of the running denominator of head n
+      f32x4 acc[HB][DBLK];
 #pragma unroll
-      for (int i = 0; i < DBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bk = 0; bk < HB; ++bk) {
+        m[bk] = -INFINITY;
+        lsum[bk] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) acc[bk][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 
       for (int tok = w * kDecodeWaveTile; tok < nt; tok += STRIDE) {
         DecodeTile<D> tl;
@@ -396,37 +409,40 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
         } else {
           load_tile<D>(tl, rk, rv, k_off, v_off, tok * D * 2);
         }
-        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 pb[HB];
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          sc[0] = mfma16(tl.k[0][kk], qb[kk], sc[0]);
-          sc[1] = mfma16(tl.k[1][kk], qb[kk], sc[1]);
+        for (int bk = 0; bk < HB; ++bk) {
+          f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int kk = 0; kk < KSTEPS; ++kk) {
+            sc[0] = mfma16(tl.k[0][kk], qb[bk][kk], sc[0]);
+            sc[1] = mfma16(tl.k[1][kk], qb[bk][kk], sc[1]);
+          }
+          // sc[bi][r] = score of token tok + 16*bi + 4*j + r for head n.
+          float s2[8];
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tt = tok + 16 * (e >> 2) + 4 * j + (e & 3);
+            s2[e] = tt < nt ? sc[e >> 2][e & 3] * sl2 : -INFINITY;
+            mx = fmaxf(mx, s2[e]);
+          }
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float m_new = fmaxf(m[bk], mx);   // finite: every tile holds a valid token
+          const float alpha = fast_exp2(m[bk] - m_new);
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const __bf16 p = (__bf16)fast_exp2(s2[e] - m_new);
+            pb[bk][e] = p;
+            ps += (float)p;   // the denominator sums exactly the weights PV uses
+          }
+          lsum[bk] = lsum[bk] * alpha + ps;
+          m[bk] = m_new;
+#pragma unroll
+          for (int i = 0; i < DBLK; ++i) acc[bk][i] *= alpha;
         }
-        // sc[bi][r] = score of token tok + 16*bi + 4*j + r for head n.
-        float s2[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tt = tok + 16 * (e >> 2) + 4 * j + (e & 3);
-          s2[e] = tt < nt ? sc[e >> 2][e & 3] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s2[e]);
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);       // finite: every tile holds a valid token
-        const float alpha = fast_exp2(m - m_new);
-        bf16x8 pb;
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 p = (__bf16)fast_exp2(s2[e] - m_new);
-          pb[e] = p;
-          ps += (float)p;   // the denominator sums exactly the weights PV uses
-        }
-        lsum = lsum * alpha + ps;
-        m = m_new;
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i) acc[i] *= alpha;
 
         wave_sync();   // the previous tile's transposed reads are done
         if (kFp8) {
@@ -450,45 +466,53 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
         for (int db = 0; db < DBLK; ++db) {
           const __bf16* base = vt + (4 * j + (L >> 2)) * PITCH + 16 * db + 4 * (L & 3);
           const bf16x8 va = concat(lds_read_tr16(base), lds_read_tr16(base + 16 * PITCH));
-          acc[db] = mfma16(va, pb, acc[db]);
+#pragma unroll
+          for (int bk = 0; bk < HB; ++bk) acc[bk][db] = mfma16(va, pb[bk], acc[bk][db]);
         }
       }
 
-      // Combine the four wavefronts' softmax states through LDS.
-      lsum += shfl_xor(lsum, 16);
-      lsum += shfl_xor(lsum, 32);
-      __syncthreads();   // every wave is done with its V tile
-      if (j == 0) {
-        cm[w * kDecodeHeadBlock + n] = m;
-        cl[w * kDecodeHeadBlock + n] = lsum;
-      }
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          co[(w * kDecodeHeadBlock + n) * OP + 16 * db + 4 * j + rr] = acc[db][rr];
-      __syncthreads();
+      // Combine the four wavefronts' softmax states through LDS, one block
+      // of 16 heads at a time.
       const int nseg = unit_segments(u.s, u.t, st.q);
       const int kseg = (int)(r - u.s / st.q);
       const size_t slot = (size_t)u.base + kseg;
-      for (int idx = threadIdx.x; idx < nh * D; idx += kThreads) {
-        const int h = idx / D;
-        const int dd = idx - h * D;
-        float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < kDecodeWaves; ++ww) M = fmaxf(M, cm[ww * kDecodeHeadBlock + h]);
-        float Ls = 0.f, Os = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kDecodeWaves; ++ww) {
-          const float wt = fast_exp2(cm[ww * kDecodeHeadBlock + h] - M);   // 0 for idle waves
-          Ls += cl[ww * kDecodeHeadBlock + h] * wt;
-          Os += co[(ww * kDecodeHeadBlock + h) * OP + dd] * wt;
+      for (int bk = 0; bk < HB; ++bk) {
+        const int nh = nh_unit - kDecodeHeadBlock * bk;
+        if (nh <= 0) break;   // uniform: the unit has fewer heads than HB blocks
+        const float lsb = lsum[bk] + shfl_xor(lsum[bk], 16);
+        const float lsw = lsb + shfl_xor(lsb, 32);
+        __syncthreads();   // every wave is done with its V tile (or the previous block's combine)
+        if (j == 0) {
+          cm[w * kDecodeHeadBlock + n] = m[bk];
+          cl[w * kDecodeHeadBlock + n] = lsw;
         }
-        if (nseg == 1) {
-          out[((size_t)u.b * hq + h_first + h) * D + dd] = Os / Ls * vsc;
-        } else {
-          part_o[(slot * kDecodeHeadBlock + h) * D + dd] = Os / Ls * vsc;
-          if (dd == 0) part_lse[slot * kDecodeHeadBlock + h] = M + __log2f(Ls);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            co[(w * kDecodeHeadBlock + n) * OP + 16 * db + 4 * j + rr] = acc[bk][db][rr];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < min(nh, kDecodeHeadBlock) * D; idx += kThreads) {
+          const int h = idx / D;
+          const int dd = idx - h * D;
+          float M = -INFINITY;
+#pragma unroll
+          for (int ww = 0; ww < kDecodeWaves; ++ww) M = fmaxf(M, cm[ww * kDecodeHeadBlock + h]);
+          float Ls = 0.f, Os = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kDecodeWaves; ++ww) {
+            const float wt = fast_exp2(cm[ww * kDecodeHeadBlock + h] - M);   // 0 for idle waves
+            Ls += cl[ww * kDecodeHeadBlock + h] * wt;
+            Os += co[(ww * kDecodeHeadBlock + h) * OP + dd] * wt;
+          }
+          const int hu = kDecodeHeadBlock * bk + h;   // head within the unit
+          if (nseg == 1) {
+            out[((size_t)u.b * hq + h_first + hu) * D + dd] = Os / Ls * vsc;
+          } else {
+            part_o[(slot * UH + hu) * D + dd] = Os / Ls * vsc;
+            if (dd == 0) part_lse[slot * UH + hu] = M + __log2f(Ls);
+          }
         }
       }
       publish_unit(unit_info, u, upb, nseg, kseg);
@@ -514,6 +538,7 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
                       float* __restrict__ out, float* __restrict__ part_o,
                       float* __restrict__ part_lse, int* __restrict__ unit_info, int batch,
                       int hq, int hkv, int g, int nhb, int tcap, int q_fixed, float scale_log2) {
+  // (one 16-head block per unit on this path: nhb is the unit count per KV head)
   constexpr int P = D + 1;          // odd pitch: column reads are conflict-free
   constexpr int CPL = D / 64;       // output columns per lane
   __shared__ float ks[kF32Tile * P];
@@ -630,7 +655,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads)
 void decode_merge(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                   const int* __restrict__ unit_info, const int32_t* __restrict__ lens,
-                  float* __restrict__ out, int hq, int hkv, int g, int nhb, int tcap) {
+                  float* __restrict__ out, int hq, int hkv, int g, int nhg, int uh, int tcap) {
   constexpr int C4 = D / 4;                  // float4 columns per row
   constexpr int ROWS = kMergeThreads / C4;   // row groups
   constexpr int U = 8;                       // rows per thread per round
@@ -646,9 +671,9 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
     return;
   }
   const int kvh = h / g;
-  const int hb = (h - kvh * g) / kDecodeHeadBlock;
-  const int hl = (h - kvh * g) - hb * kDecodeHeadBlock;
-  const size_t unit = ((size_t)b * hkv + kvh) * nhb + hb;
+  const int hg = (h - kvh * g) / uh;         // unit of uh consecutive heads
+  const int hl = (h - kvh * g) - hg * uh;    // head within the unit
+  const size_t unit = ((size_t)b * hkv + kvh) * nhg + hg;
   const int base = unit_info[2 * unit];
   const int ns = unit_info[2 * unit + 1];
   if (ns <= 1) return;   // written directly by its only segment
@@ -666,7 +691,7 @@ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ pa
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * ROWS;
-      const size_t row = ((size_t)base + s) * kDecodeHeadBlock + hl;
+      const size_t row = ((size_t)base + s) * uh + hl;
       lr[u] = -INFINITY;
       ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < ns) {   // padding rows load nothing
@@ -717,8 +742,9 @@ DecodeWorkspace decode_workspace_layout(const DecodeShape& s) {
   DecodeWorkspace w;
   w.info_offset = 0;
   w.lse_offset = up((int64_t)s.units * 2 * 4);
-  w.o_offset = w.lse_offset + up(s.max_slots * kDecodeHeadBlock * 4);
-  w.total = w.o_offset + up(s.max_slots * kDecodeHeadBlock * (int64_t)s.d * 4);
+  const int64_t uh = (int64_t)kDecodeHeadBlock * s.hb;   // heads per unit: the width of a partial row
+  w.o_offset = w.lse_offset + up(s.max_slots * uh * 4);
+  w.total = w.o_offset + up(s.max_slots * uh * (int64_t)s.d * 4);
   return w;
 }
 
@@ -727,7 +753,6 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
                                hipStream_t stream, const PagedKV& paged, const float* k_scale,
                                const float* v_scale) {
   const int g = s.hq / s.hkv;
-  const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
   const DecodeWorkspace wl = decode_workspace_layout(s);
   int* info = reinterpret_cast<int*>(workspace + wl.info_offset);
   float* plse = reinterpret_cast<float*>(workspace + wl.lse_offset);
@@ -737,30 +762,37 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
   const float sl2 = s.scale * kLog2e;
   if (s.dtype == 1 || s.dtype == 2) {
     auto qp = static_cast<const __bf16*>(q);
-#define GQA_SPLIT(DD, PG, F8)                                                                          \
-  hipLaunchKernelGGL((decode_split_bf16<DD, PG, F8>), grid, block, 0, stream, qp, k, v, lens, out, po, plse, \
-                     info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2, paged, k_scale, v_scale)
+#define GQA_SPLIT2(DD, PG, F8, HB)                                                                       \
+  hipLaunchKernelGGL((decode_split_bf16<DD, PG, F8, HB>), grid, block, 0, stream, qp, k, v, lens, out, po, plse, \
+                     info, s.batch, s.hq, s.hkv, g, s.nhg, s.tcap, s.q_fixed, sl2, paged, k_scale, v_scale)
+#define GQA_SPLIT(DD, PG, F8)        \
+  if (s.hb == 2) {                   \
+    GQA_SPLIT2(DD, PG, F8, 2);       \
+  } else {                           \
+    GQA_SPLIT2(DD, PG, F8, 1);       \
+  }
     if (s.dtype == 2) {
-      if (s.d == 128) GQA_SPLIT(128, false, true);
-      else GQA_SPLIT(64, false, true);
+      if (s.d == 128) { GQA_SPLIT(128, false, true) }
+      else { GQA_SPLIT(64, false, true) }
     } else if (paged.table != nullptr) {
-      if (s.d == 128) GQA_SPLIT(128, true, false);
-      else GQA_SPLIT(64, true, false);
+      if (s.d == 128) { GQA_SPLIT(128, true, false) }
+      else { GQA_SPLIT(64, true, false) }
     } else {
-      if (s.d == 128) GQA_SPLIT(128, false, false);
-      else GQA_SPLIT(64, false, false);
+      if (s.d == 128) { GQA_SPLIT(128, false, false) }
+      else { GQA_SPLIT(64, false, false) }
     }
 #undef GQA_SPLIT
+#undef GQA_SPLIT2
   } else {
     auto qp = static_cast<const float*>(q);
     auto kp = static_cast<const float*>(k);
     auto vp = static_cast<const float*>(v);
     if (s.d == 128)
       hipLaunchKernelGGL(decode_split_f32<128>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
+                         plse, info, s.batch, s.hq, s.hkv, g, s.nhg, s.tcap, s.q_fixed, sl2);
     else
       hipLaunchKernelGGL(decode_split_f32<64>, grid, block, 0, stream, qp, kp, vp, lens, out, po,
-                         plse, info, s.batch, s.hq, s.hkv, g, nhb, s.tcap, s.q_fixed, sl2);
+                         plse, info, s.batch, s.hq, s.hkv, g, s.nhg, s.tcap, s.q_fixed, sl2);
   }
   return hipGetLastError();
 }
@@ -768,7 +800,6 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
 hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* workspace,
                                const DecodeShape& s, hipStream_t stream) {
   const int g = s.hq / s.hkv;
-  const int nhb = (g + kDecodeHeadBlock - 1) / kDecodeHeadBlock;
   const DecodeWorkspace wl = decode_workspace_layout(s);
   const int* info = reinterpret_cast<const int*>(workspace + wl.info_offset);
   const float* plse = reinterpret_cast<const float*>(workspace + wl.lse_offset);
@@ -776,10 +807,10 @@ hipError_t launch_decode_merge(const int32_t* lens, float* out, const char* work
   const dim3 grid(s.hq, s.batch);
   if (s.d == 128)
     hipLaunchKernelGGL(decode_merge<128>, grid, dim3(kMergeThreads), 0, stream, po, plse, info, lens,
-                       out, s.hq, s.hkv, g, nhb, s.tcap);
+                       out, s.hq, s.hkv, g, s.nhg, kDecodeHeadBlock * s.hb, s.tcap);
   else
     hipLaunchKernelGGL(decode_merge<64>, grid, dim3(kMergeThreads), 0, stream, po, plse, info, lens,
-                       out, s.hq, s.hkv, g, nhb, s.tcap);
+                       out, s.hq, s.hkv, g, s.nhg, kDecodeHeadBlock * s.hb, s.tcap);
   return hipGetLastError();
 }
 

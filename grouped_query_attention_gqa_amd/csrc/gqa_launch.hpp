@@ -6,8 +6,10 @@
 
 namespace gqa {
 
-// Query heads handled by one decode workgroup: the MFMA column block.  Groups
-// of up to 16 query heads share a single pass over their KV head.
+// Query heads of one MFMA column block in decode.  A decode unit covers one
+// block, or two (32 heads) for bf16 and E4M3 caches when the group is larger
+// than 16, so groups of up to 32 query heads share a single pass over their
+// KV head.
 constexpr int kDecodeHeadBlock = 16;
 // Decode: tokens per wavefront iteration (bf16 path) and waves per workgroup.
 constexpr int kDecodeWaveTile = 32;
@@ -24,7 +26,9 @@ constexpr int kPersistentWorkgroups = GQA_DECODE_GRID;
 
 struct DecodeShape {
   int batch, hq, hkv, d, tcap;
-  int units;         // batch * hkv * ceil(g / 16)
+  int hb;            // 16-head blocks per unit: 2 for bf16 and E4M3 caches when g > 16, else 1
+  int nhg;           // units per KV head: ceil(ceil(g / 16) / hb)
+  int units;         // batch * hkv * nhg
   int q_fixed;       // tokens per range fixed by the caller, 0 = chosen on the device
   int grid;          // workgroups launched
   int64_t max_slots; // upper bound on partial slots (ranges + units)
@@ -33,8 +37,8 @@ struct DecodeShape {
 };
 
 // Byte offsets of the workspace arrays: per-unit (first slot, segment
-// count), then per-slot log2-sum-exp [slots][16], then per-slot normalised
-// outputs [slots][16][d], each 256-byte aligned.
+// count), then per-slot log2-sum-exp [slots][16 hb], then per-slot
+// normalised outputs [slots][16 hb][d], each 256-byte aligned.
 struct DecodeWorkspace {
   int64_t info_offset, lse_offset, o_offset, total;
 };

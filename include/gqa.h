@@ -79,7 +79,8 @@ const char* gqa_last_hip_error(void);
 
 /*
  * Launch plan of a decode call.  Decode lays the cached tokens of every
- * (sequence, KV head, block of up to 16 query heads) end to end into one
+ * (sequence, KV head, block of up to 16 query heads; up to 32 for bf16 and
+ * E4M3 caches when the group has more than 16) end to end into one
  * stream and cuts it into equal ranges, one per workgroup, so ragged batches
  * stay balanced; a range's piece inside one sequence is attended by one
  * workgroup for all query heads of the group, and a sequence that spans
@@ -103,11 +104,10 @@ int32_t gqa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
  * Workspace bytes that cover gqa_decode (and its two stages) for every
  * number of KV heads that divides num_q_heads, every dtype and automatic
  * ranges (split_tokens = 0), given only the batch, the query heads, the head
- * dimension and the cache capacity.  It is the size gqa_decode_plan reports
- * for the shape with the most units (num_kv_heads = num_q_heads), which
- * bounds every other grouping because a decode unit never covers fewer than
- * one query head.  Returns 0 when the arguments are invalid (a size below 1,
- * head_dim not 64 or 128, or a size overflow).  Pure host arithmetic.
+ * dimension and the cache capacity: the largest size gqa_decode_plan reports
+ * over those KV-head counts.  Returns 0 when the arguments are invalid (a
+ * size below 1, head_dim not 64 or 128, or a size overflow).  Pure host
+ * arithmetic.
  */
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len);

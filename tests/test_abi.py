@@ -73,13 +73,15 @@ def test_status_str_matches_status_string(lib):
 
 def test_workspace_bytes_cover_every_grouping():
     for (B, hq, d, tcap) in [(32, 32, 128, 8192), (64, 32, 128, 32768), (4, 16, 128, 131072),
-                             (1, 8, 64, 256), (3, 71, 128, 320), (2, 12, 64, 1)]:
+                             (1, 8, 64, 256), (3, 71, 128, 320), (2, 12, 64, 1), (1, 128, 128, 65536),
+                             (2, 96, 64, 4096)]:
         bound = gqa.gqa_decode_workspace_bytes(B, hq, d, tcap)
         assert bound > 0
         for hkv in [h for h in range(1, hq + 1) if hq % h == 0]:
             for dt in (F32, BF16, 2):
                 assert gqa.gqa_decode_plan(B, hq, hkv, d, tcap, dt).workspace_bytes <= bound, (B, hq, hkv, d)
-        assert gqa.gqa_decode_plan(B, hq, hq, d, tcap, BF16).workspace_bytes == bound
+        assert max(gqa.gqa_decode_plan(B, hq, hkv, d, tcap, BF16).workspace_bytes
+                   for hkv in range(1, hq + 1) if hq % hkv == 0) == bound
 
 
 @pytest.mark.parametrize("args", [(0, 8, 64, 256), (1, 0, 64, 256), (1, 8, 96, 256), (1, 8, 64, 0)])
@@ -107,9 +109,13 @@ def test_plan_auto_and_explicit():
     assert one.workgroups == 2                              # 2 units x 256 tokens, 256-token minimum
     e = gqa.gqa_decode_plan(2, 4, 1, 64, 1000, BF16, split_tokens=128)
     assert e.range_tokens == 128 and e.workgroups == 16     # ceil(2 * 1000 / 128)
-    # 71 query heads on one KV head: 5 blocks of 16 heads, each its own unit
+    # 71 query heads on one KV head: 5 blocks of 16 heads; a bf16 unit holds two
+    # blocks (32 heads read one pass of K/V), so 3 units; fp32 keeps one block per unit
     big = gqa.gqa_decode_plan(1, 71, 1, 128, 4096, BF16, split_tokens=4096)
-    assert big.workgroups == 5
+    assert big.workgroups == 3
+    assert gqa.gqa_decode_plan(1, 71, 1, 128, 4096, F32, split_tokens=4096).workgroups == 5
+    assert gqa.gqa_decode_plan(1, 32, 1, 128, 4096, BF16, split_tokens=4096).workgroups == 1
+    assert gqa.gqa_decode_plan(1, 16, 1, 128, 4096, BF16, split_tokens=4096).workgroups == 1
 
 
 @pytest.mark.parametrize("args,status", [

@@ -62,7 +62,11 @@ SMALL_CASES = [
     ("bf16", 2, 8, 2, 64, [77, 640], 640, 128),
     ("bf16", 2, 4, 4, 128, [500, 129], 512, 128),       # MHA endpoint
     ("bf16", 2, 16, 1, 128, [700, 31], 704, 192),       # MQA, group 16
-    ("bf16", 1, 71, 1, 128, [300], 320, 64),            # 71 heads on one KV head (5 head blocks)
+    ("bf16", 1, 71, 1, 128, [300], 320, 64),            # 71 heads on one KV head (5 blocks in 3 units)
+    ("bf16", 2, 32, 1, 128, [900, 17], 960, 0),         # group 32: two full blocks share one unit
+    ("bf16", 2, 40, 2, 64, [700, 1300], 1344, 128),     # group 20: a full block and a 4-head block
+    ("bf16", 1, 48, 1, 128, [2000], 2048, 0),           # group 48: a two-block unit and a one-block unit
+    ("bf16", 2, 128, 2, 128, [3000, 64], 3072, 0),      # group 64: two units of two blocks per KV head
     ("bf16", 2, 32, 2, 128, [4096, 1500], 4096, 0),     # group 16, wide
     ("bf16", 3, 6, 2, 64, [0, 5, 64], 64, 0),           # empty sequence
     ("f32", 2, 8, 2, 64, [1, 300], 320, 64),
@@ -167,7 +171,8 @@ def _mapping_probe(B, Hq, Hkv, T, split):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,T", [(32, 32, 8, 8192), (4, 16, 1, 4096), (3, 71, 1, 64), (2, 6, 2, 128)])
+@pytest.mark.parametrize("B,Hq,Hkv,T", [(32, 32, 8, 8192), (4, 16, 1, 4096), (3, 71, 1, 64), (2, 6, 2, 128),
+                                           (2, 96, 2, 256), (2, 40, 1, 128)])
 def test_mapping_probe_bit_exact(B, Hq, Hkv, T):
     need_gpu()
     say("mapping probe", B, Hq, Hkv, T)

@@ -46,6 +46,8 @@ CASES = [
     (4, 8, 2, 64, [0, 5, 129, 64], 192, 64),
     (2, 32, 2, 128, [2000, 513], 2048, 256),
     (1, 71, 1, 128, [333], 512, 64),
+    (2, 64, 2, 128, [1500, 40], 1536, 0),     # group 32: two head blocks per unit
+    (2, 40, 1, 64, [700, 129], 768, 128),     # group 40: a two-block unit and an 8-head unit
     (2, 12, 3, 64, [33, 250], 256, 0),
 ]
 

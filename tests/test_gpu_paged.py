@@ -52,6 +52,8 @@ CASES = [
     (2, 32, 2, 128, [2000, 513], 2048, 256),
     (1, 4, 4, 128, [97], 128, 1),          # one token per page
     (2, 12, 3, 64, [33, 250], 256, 8),     # group 4 of 12, pages smaller than a tile
+    (2, 64, 2, 128, [1000, 333], 1024, 16),  # group 32: two head blocks per unit
+    (1, 48, 1, 64, [777], 800, 32),        # group 48: a two-block unit and a one-block unit
 ]
 
 
