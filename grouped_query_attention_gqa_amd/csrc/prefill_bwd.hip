@@ -20,22 +20,28 @@
 //    tiles of keys up to its diagonal through LDS and accumulates dQ^T in
 //    registers.  Its prologue forms D for its rows from out and dO and
 //    stores it, with lse in the log2 domain, for the second kernel.
-//  * prefill_bwd_dkdv: a workgroup owns 128 keys of one KV head (32 per
-//    wavefront, with K and V held in registers as MFMA operands) and
-//    streams, through double-buffered LDS, the Q/dO tiles of every query
-//    head of the group at every position from its first key on.  dK and dV
-//    of the KV head are summed over the g heads in registers: per-head
-//    gradients never reach memory and the shared K/V rows are never copied.
-//    Q tiles are visited from the last one down, so all workgroups of one
-//    KV head start on the same tile and move through Q/dO together, and
-//    workgroups are issued heaviest (first keys) first, one KV head's
-//    workgroups on one XCD when the KV-head count allows.
+//  * prefill_bwd_dkdv: a workgroup owns two 128-key tiles of one KV head,
+//    p and the mirror tile from the end (32 keys per wavefront, with K and
+//    V held in registers as MFMA operands), one after the other.  For each
+//    it streams, through double-buffered LDS, the Q/dO tiles of every query
+//    head of the group at every position from the tile's first key on.  dK
+//    and dV of the KV head are summed over the g heads in registers:
+//    per-head gradients never reach memory and the shared K/V rows are
+//    never copied.  The two tiles of a pair cover the same number of Q
+//    tiles whatever p, so one round of equal workgroups (one per CU, at
+//    512 registers per lane) covers the sequence; the first tile is swept
+//    from the last Q tile down and the second from its diagonal up, so all
+//    workgroups of one KV head, placed on one XCD when the KV-head count
+//    allows, read the same one or two Q tiles at any time and share them
+//    in L2.
 //
 // Layouts: q, dout, out [B, Hq, N, d]; k, v [B, Hkv, N, d]; lse [B, Hq, N];
 // row_terms [2][B, Hq, N] (lse * log2 e, then D); dq [B, Hq, N, d]; dk, dv
 // [B, Hkv, N, d].  MFMA operand
 // layouts are the ones listed in gqa_device.hpp; LDS tiles are those of
 // prefill_tiles.hpp.
+
+#include <type_traits>
 
 #include "gqa_device.hpp"
 #include "gqa_launch.hpp"
@@ -231,9 +237,15 @@ void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 template <int D>
 __device__ __forceinline__ void issue_rows(const tiles::TileFill<D>& fill, const __bf16* qh,
                                            const __bf16* oh, const float* scalars, __bf16* qs, __bf16* os,
-                                           float* rs, int n, int w, int row0, int lane) {
+                                           float* rs, int n, int w, int row0) {
   fill.issue2(qs, make_rsrc(qh, n * D * 2), os, make_rsrc(oh, n * D * 2), w, row0);
-  if (w < 2) tiles::load_floats_lds(rs + w * kTile, make_rsrc(scalars, n * 4), (row0 + lane) * 4);
+  if (w < 2) {
+    // the lane index is recomputed here rather than kept live across the
+    // step (under the step's register pressure it would be spilled)
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    tiles::load_floats_lds(rs + w * kTile, make_rsrc(scalars, n * 4), (row0 + lane) * 4);
+  }
 }
 
 // P^T and dS^T of one 32-row block as bf16 A operands (lane = key, k-group
@@ -397,23 +409,22 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
   __shared__ __align__(16) float r0s[2 * kTile];   // lse, then D, of the stage's rows
   __shared__ __align__(16) float r1s[2 * kTile];
 
-  int unit, kt;
-  unit_and_tile(blockIdx.x, units, unit, kt);
+  int unit, pair;
+  unit_and_tile(blockIdx.x, units, unit, pair);
   const int b = unit / hkv;
   const int kvh = unit - b * hkv;
-  const int k0 = kt * kKeys;
+  const int n_ktiles = (n + kKeys - 1) / kKeys;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // this lane's key within the wave (A row / D row index)
   const int j = lane >> 5;     // contraction group
-  const int kw = k0 + 32 * w;  // the wave's first key
 
   // K and V rows of key kw + col as B operands of S = Q K^T and dP = dO V^T.
   const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
   bf16x8 kb[KSTEPS], vb[KSTEPS];
-  {
+  auto load_kv = [&](int kw) {
     const int key = kw + col;
     const __bf16* krow = k + kv_off + (size_t)min(key, n - 1) * D;
     const __bf16* vrow = v + kv_off + (size_t)min(key, n - 1) * D;
@@ -423,7 +434,7 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
       vb[kk] = load_bf16x8(vrow + 16 * kk + 8 * j);
       if (key >= n) kb[kk] = vb[kk] = bf16x8{};
     }
-  }
+  };
 
   int a_rd[2][KSTEPS];           // Q / dO rows 32 rb + col, chunk 2 kk + j
   int t_rd[4][DB], t_dx[4][DB];  // Q^T / dO^T: rows of 16-row chunk c, columns of block db
@@ -452,87 +463,135 @@ void prefill_bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k
   }
 
   f32x16 dka[DB], dva[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) dka[i] = dva[i] = f32x16{};
-
-  // Steps: q-tiles from the last down to the one holding key k0, each for
-  // the g query heads of the group.
   const int qt_last = (n - 1) / kTile;
-  const int qt_first = k0 / kTile;
-  const int nsteps = (qt_last - qt_first + 1) * g;
   const tiles::TileFill<D> fill(tid);
 
-  // Loads of step s into one stage: the Q and dO tiles, and one float per
-  // lane from waves 0 (lse) and 1 (D), zeros past n.
-  auto issue = [&](int s, __bf16* qs, __bf16* os, float* rs) {
-    const int qt = qt_last - s / g;
+  // Loads of step s of a sweep into one stage: the Q and dO tiles of q-tile
+  // qt, and one float per lane from waves 0 (lse) and 1 (D), zeros past n.
+  auto issue = [&](int s, int qt, __bf16* qs, __bf16* os, float* rs) {
     const size_t hrow = ((size_t)b * hq + kvh * g + s % g) * n;
     issue_rows<D>(fill, q + hrow * D, dout + hrow * D, row_terms + (w == 1 ? rows : 0) + hrow, qs, os, rs, n, w,
-                  qt * kTile, lane);
-  };
-
-  // Only the last two q-tiles (the last 2 g steps) reach below a key of the
-  // workgroup and need the causal mask; every earlier step runs the
-  // mask-free body, in a loop of its own so that the accumulators never
-  // cross a branch.  Rows past n need no mask either: their q, dout, lse and
-  // D arrive as zeros, so their P = 1 meets zero dout and zero dS.
-  const int n_plain = nsteps - min(nsteps, 2 * g);
-  auto plain = [&](const __bf16* qs, const __bf16* os, const float* rs) {
-    dkdv_step<D, false>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, 0);
-  };
-  auto masked = [&](int s, const __bf16* qs, const __bf16* os, const float* rs) {
-    const int i0 = (qt_last - s / g) * kTile;
-    if (i0 + kTile - 1 < kw) return;   // every row of the tile precedes the wave's keys
-    dkdv_step<D, true>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, kw + col - i0);
+                  qt * kTile);
   };
   auto sync = [&]() {
     __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next step have landed
     __syncthreads();                 // ... everyone's, and everyone is done with the current stage
   };
-
-  // Stage 0 holds even steps, stage 1 odd ones.
-  issue(0, q0s, o0s, r0s);
-  sync();
-  int s = 0;
-  for (; s + 1 < n_plain; s += 2) {
-    issue(s + 1, q1s, o1s, r1s);
-    plain(q0s, o0s, r0s);
-    sync();
-    if (s + 2 < nsteps) issue(s + 2, q0s, o0s, r0s);
-    plain(q1s, o1s, r1s);
-    sync();
-  }
-  if (s < n_plain) {
-    if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
-    plain(q0s, o0s, r0s);
-    sync();
-    ++s;
-  }
-  for (; s < nsteps; ++s) {
-    if (s & 1) {
-      if (s + 1 < nsteps) issue(s + 1, q0s, o0s, r0s);
-      masked(s, q1s, o1s, r1s);
-    } else {
-      if (s + 1 < nsteps) issue(s + 1, q1s, o1s, r1s);
-      masked(s, q0s, o0s, r0s);
-    }
-    sync();
-  }
-
-  // D rows of dK/dV: key kw + 8 (r/4) + 4 j + r%4, column 32 db + col.
   float* dk_b = dk + kv_off;
   float* dv_b = dv + kv_off;
+
+  // One key tile: the q-tiles from the one holding its first key to the
+  // last, each for the g query heads of the group, visited downward
+  // (UP false) or upward.  Only the two q-tiles at the diagonal (2 g steps:
+  // the last of a downward sweep, the first of an upward one) reach below a
+  // key of the workgroup and need the causal mask; every other step runs the
+  // mask-free body, in a loop of its own so that the accumulators never
+  // cross a branch.  Rows past n need no mask either: their q, dout, lse and
+  // D arrive as zeros, so their P = 1 meets zero dout and zero dS.  Stage 0
+  // holds even steps, stage 1 odd ones.
+  auto sweep = [&](int kt, auto upward) {
+    constexpr bool UP = decltype(upward)::value;
+    const int kw = kt * kKeys + 32 * w;   // the wave's first key
+    const int qt_first = kt * kKeys / kTile;
+    const int nsteps = (qt_last - qt_first + 1) * g;
+    auto qt_of = [&](int s) { return UP ? qt_first + s / g : qt_last - s / g; };
+    auto plain = [&](const __bf16* qs, const __bf16* os, const float* rs) {
+      dkdv_step<D, false>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, 0);
+    };
+    auto masked = [&](int s, const __bf16* qs, const __bf16* os, const float* rs) {
+      const int i0 = qt_of(s) * kTile;
+      if (i0 + kTile - 1 < kw) return;   // every row of the tile precedes the wave's keys
+      dkdv_step<D, true>(qs, os, rs, kb, vb, a_rd, t_rd, t_dx, dka, dva, scale_log2, j, kw + col - i0);
+    };
+    auto masked_steps = [&](int& s, int end) {
+      for (; s < end; ++s) {
+        if (s & 1) {
+          if (s + 1 < nsteps) issue(s + 1, qt_of(s + 1), q0s, o0s, r0s);
+          masked(s, q1s, o1s, r1s);
+        } else {
+          if (s + 1 < nsteps) issue(s + 1, qt_of(s + 1), q1s, o1s, r1s);
+          masked(s, q0s, o0s, r0s);
+        }
+        sync();
+      }
+    };
+    // the same for an even s on entry and an even count, two steps per trip
+    auto masked_pairs = [&](int& s, int end) {
+      for (; s + 1 < end; s += 2) {
+        issue(s + 1, qt_of(s + 1), q1s, o1s, r1s);
+        masked(s, q0s, o0s, r0s);
+        sync();
+        if (s + 2 < nsteps) issue(s + 2, qt_of(s + 2), q0s, o0s, r0s);
+        masked(s + 1, q1s, o1s, r1s);
+        sync();
+      }
+    };
+    // plain steps s .. end - 1, s even on entry
+    auto plain_steps = [&](int& s, int end) {
+      for (; s + 1 < end; s += 2) {
+        issue(s + 1, qt_of(s + 1), q1s, o1s, r1s);
+        plain(q0s, o0s, r0s);
+        sync();
+        if (s + 2 < nsteps) issue(s + 2, qt_of(s + 2), q0s, o0s, r0s);
+        plain(q1s, o1s, r1s);
+        sync();
+      }
+      if (s < end) {
+        if (s + 1 < nsteps) issue(s + 1, qt_of(s + 1), q1s, o1s, r1s);
+        plain(q0s, o0s, r0s);
+        sync();
+        ++s;
+      }
+    };
+
+    __builtin_amdgcn_sched_barrier(0);   // the previous sweep's stores go first
+    issue(0, qt_of(0), q0s, o0s, r0s);
+    load_kv(kw);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = kw + 8 * (r >> 2) + 4 * j + (r & 3);
-    if (key < n) {
+    for (int i = 0; i < DB; ++i) dka[i] = dva[i] = f32x16{};
+    sync();
+    const int n_mask = min(nsteps, 2 * g);   // even whenever plain steps follow it
+    int s = 0;
+    if (UP) {
+      masked_pairs(s, n_mask);
+      if (s < n_mask) {   // an odd count: the sweep's one q-tile with g odd, s even here
+        if (s + 1 < nsteps) issue(s + 1, qt_of(s + 1), q1s, o1s, r1s);
+        masked(s, q0s, o0s, r0s);
+        sync();
+        ++s;
+      }
+      plain_steps(s, nsteps);
+    } else {
+      plain_steps(s, nsteps - n_mask);
+      masked_steps(s, nsteps);
+    }
+
+    // D rows of dK/dV: key kw + 8 (r/4) + 4 j + r%4, column 32 db + col.
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dk_b[(size_t)key * D + 32 * db + col] = dka[db][r] * scale;
-        dv_b[(size_t)key * D + 32 * db + col] = dva[db][r];
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw + 8 * (r >> 2) + 4 * j + (r & 3);
+      if (key < n) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dk_b[(size_t)key * D + 32 * db + col] = dka[db][r] * scale;
+          dv_b[(size_t)key * D + 32 * db + col] = dva[db][r];
+        }
       }
     }
-  }
+  };
+
+  // A workgroup owns key tiles `pair` and n_ktiles - 1 - `pair`, whose sweeps
+  // hold n_ktiles + 1 q-tiles between them whatever the pair (for 128-key
+  // tiles and 64-row q-tiles), so one round of workgroups covers the
+  // sequence with equal work each.  The first sweep runs downward from the
+  // last q-tile and the second upward from its diagonal: every down-sweep
+  // reads q-tile qt_last - t at its t-th q-tile and every up-sweep, which
+  // starts as its workgroup's down-sweep ends, reads q-tile t - 2 then, so
+  // the workgroups of one KV head read the same one or two q-tiles at a time
+  // and share them in L2.
+  sweep(pair, std::integral_constant<bool, false>{});
+  const int kt2 = n_ktiles - 1 - pair;
+  if (kt2 > pair) sweep(kt2, std::integral_constant<bool, true>{});
 }
 
 }  // namespace
@@ -547,6 +606,7 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   const int dq_units = s.batch * s.hkv * (g / gw);
   const int kv_units = s.batch * s.hkv;
   const int n_ktiles = (s.n + kKeys - 1) / kKeys;
+  const int n_pairs = (n_ktiles + 1) / 2;   // key tiles p and n_ktiles - 1 - p per workgroup
   const size_t rows = (size_t)s.batch * s.hq * s.n;
   const float sl2 = s.scale * kLog2e;
   auto qp = static_cast<const __bf16*>(q);
@@ -555,7 +615,7 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   auto op = static_cast<const __bf16*>(dout);
   const dim3 block(kThreads);
   const dim3 grid_dq((unsigned)dq_units * (unsigned)n_qtiles);
-  const dim3 grid_kv((unsigned)kv_units * (unsigned)n_ktiles);
+  const dim3 grid_kv((unsigned)kv_units * (unsigned)n_pairs);
   if (s.d == 128) {
     hipLaunchKernelGGL(prefill_bwd_dq<128>, grid_dq, block, 0, stream, qp, kp, vp, out, lse, op, dq, row_terms,
                        rows, s.hq, s.hkv, s.n, g, gw, n_qtiles, dq_units, sl2, s.scale);
