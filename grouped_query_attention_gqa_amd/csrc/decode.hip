@@ -11,8 +11,8 @@
 // query heads act as extra query rows against the shared K/V).
 //
 // Work partition (balanced "stream" split).  A unit is one (sequence, KV
-// head, block of 16 query heads); its work is the sequence's T_b cached
-// tokens.  The units' tokens are laid end to end into one stream of W
+// head, block of 16 query heads, or two blocks for bf16 and E4M3 caches
+// when the group is wider); its work is the sequence's T_b cached tokens.  The units' tokens are laid end to end into one stream of W
 // token-units, and range r of the stream is [r*Q, (r+1)*Q): every range has
 // the same size no matter how ragged the lengths are, and about one range
 // runs per resident workgroup, so no workgroup idles at the tail.  Q is
@@ -21,7 +21,11 @@
 // falls inside one unit is a segment; a unit split over n > 1 segments gets
 // n partial results (normalised O and log2-sum-exp) that decode_merge
 // combines, and a unit covered by a single segment is written straight to
-// the output.
+// the output.  Every workgroup derives the geometry itself before its first
+// load, so this prologue is kept short: up to 64 sequences, each wavefront
+// scans the lengths with wavefront shuffles (no barrier), and the floor
+// divisions by Q go through a double reciprocal with one exact correction
+// instead of 64-bit integer division.
 //
 // bf16 path, per wavefront and 32-token tile:
 //   S^T[32 tok, 16 heads] = K[32, d] Q^T[d, 16]      v_mfma_f32_16x16x32_bf16
@@ -51,9 +55,27 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int tcap) {
   return t < 0 ? 0 : (t > tcap ? tcap : t);
 }
 
+// Stream geometry shared by every workgroup of a launch.
+struct Stream {
+  long long w;        // total token-units
+  long long q;        // tokens per range
+  long long ranges;   // number of ranges
+  double qinv;        // 1 / q, for the floor divisions by q
+};
+
+// floor(x / q) for 0 <= x < W: the plan keeps the range count (about W / q)
+// below 2^27, so the double quotient is within one of the true one and the
+// remainder's sign fixes it.
+__device__ __forceinline__ long long range_div(long long x, const Stream& st) {
+  long long d = (long long)((double)x * st.qinv);
+  const long long r = x - d * st.q;
+  d += (r >= st.q) - (r < 0);
+  return d;
+}
+
 // Segments of a unit occupying stream positions [s, s + t).
-__device__ __forceinline__ int unit_segments(long long s, int t, long long q) {
-  return t == 0 ? 0 : (int)((s + t - 1) / q - s / q + 1);
+__device__ __forceinline__ int unit_segments(long long s, int t, const Stream& st) {
+  return t == 0 ? 0 : (int)(range_div(s + t - 1, st) - range_div(s, st) + 1);
 }
 
 // A unit of the stream: sequence b, unit j within the sequence (kvh * nhb +
@@ -63,12 +85,6 @@ struct Unit {
   long long s;
 };
 
-// Stream geometry shared by every workgroup of a launch.
-struct Stream {
-  long long w;        // total token-units
-  long long q;        // tokens per range
-  long long ranges;   // number of ranges
-};
 
 // Every workgroup scans the lengths (two block-wide scans over the batch)
 // so that any stream position maps to its unit and partial-slot index.
@@ -105,8 +121,95 @@ __device__ __forceinline__ void seq_block(int batch, int& b0, int& b1) {
   b1 = min(batch, b0 + per);
 }
 
+__device__ __forceinline__ long long readlane64(long long v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(unsigned)(unsigned long long)v, l);
+  const int hi = __builtin_amdgcn_readlane((int)((unsigned long long)v >> 32), l);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// The geometry and units are the same in every lane; saying so keeps them in
+// scalar registers (buffer resources built from them stay scalar).
+__device__ __forceinline__ Stream uniform_stream(Stream st) {
+  st.w = uniform64(st.w);
+  st.q = uniform64(st.q);
+  st.ranges = uniform64(st.ranges);
+  st.qinv = __longlong_as_double(uniform64(__double_as_longlong(st.qinv)));
+  return st;
+}
+__device__ __forceinline__ Unit uniform_unit(Unit u) {
+  u.b = __builtin_amdgcn_readfirstlane(u.b);
+  u.j = __builtin_amdgcn_readfirstlane(u.j);
+  u.t = __builtin_amdgcn_readfirstlane(u.t);
+  u.base = __builtin_amdgcn_readfirstlane(u.base);
+  u.s = uniform64(u.s);
+  return u;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Up to 64 sequences: every wavefront computes the geometry by itself with
+// wavefront scans (lane b owns sequence b), so no barrier is needed.  Each
+// wavefront keeps its lanes' sequence start, slot base and length in LDS
+// (the same values from every wavefront) for stream_locate.
+__device__ Stream stream_setup_wave(ScanSmem& sm, const int32_t* lens, int batch, int upb, int tcap,
+                                    int q_fixed) {
+  const int lane = threadIdx.x & 63;
+  const int t = lane < batch ? clamp_len(lens, lane, tcap) : 0;
+  const long long span = (long long)t * upb;
+  const long long incl = wave_inclusive_scan(span);
+  Stream st;
+  st.w = readlane64(incl, 63);
+  if (q_fixed > 0) {
+    st.q = q_fixed;
+  } else {
+    st.q = (st.w + gridDim.x - 1) / gridDim.x;
+    if (st.q < kMinRange) st.q = kMinRange;
+  }
+  st.ranges = (st.w + st.q - 1) / st.q;
+  st.qinv = 1.0 / (double)st.q;
+  long long s = incl - span;
+  int segs = 0;
+  for (int j = 0; j < upb; ++j, s += t) segs += unit_segments(s, t, st);
+  const int sincl = wave_inclusive_scan(segs);
+  sm.tok[lane] = incl - span;
+  sm.tok[64 + lane] = t;
+  sm.seg[lane] = sincl - segs;
+  return st;
+}
+
+__device__ Unit stream_locate_wave(ScanSmem& sm, int upb, const Stream& st, long long x) {
+  const int lane = threadIdx.x & 63;
+  const long long s_b = sm.tok[lane];
+  const int t = (int)sm.tok[64 + lane];
+  const int base_b = sm.seg[lane];
+  const unsigned long long hit = __ballot(t > 0 && x >= s_b && x < s_b + (long long)t * upb);
+  const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);   // one lane holds x
+  const long long s = readlane64(s_b, l);
+  const int tb = __builtin_amdgcn_readlane(t, l);
+  int base = __builtin_amdgcn_readlane(base_b, l);
+  const int j = (int)((x - s) / tb);
+  for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * tb, tb, st);
+  return Unit{l, j, tb, base, s + (long long)j * tb};
+}
+
 __device__ Stream stream_setup(ScanSmem& sm, const int32_t* lens, int batch, int upb, int tcap,
                                int q_fixed) {
+  if (batch <= 64) return uniform_stream(stream_setup_wave(sm, lens, batch, upb, tcap, q_fixed));
   int b0, b1;
   seq_block(batch, b0, b1);
   long long mine = 0;
@@ -120,20 +223,22 @@ __device__ Stream stream_setup(ScanSmem& sm, const int32_t* lens, int batch, int
     if (st.q < kMinRange) st.q = kMinRange;
   }
   st.ranges = (st.w + st.q - 1) / st.q;
+  st.qinv = 1.0 / (double)st.q;
   // segment counts, now that every unit's first position is known
   long long s = sm.tok[threadIdx.x];
   int segs = 0;
   for (int b = b0; b < b1; ++b) {
     const int t = clamp_len(lens, b, tcap);
-    for (int j = 0; j < upb; ++j, s += t) segs += unit_segments(s, t, st.q);
+    for (int j = 0; j < upb; ++j, s += t) segs += unit_segments(s, t, st);
   }
   block_exclusive_scan(sm.seg, segs);
-  return st;
+  return uniform_stream(st);
 }
 
 // The non-empty unit holding stream position x (0 <= x < w).
 __device__ Unit stream_locate(ScanSmem& sm, const int32_t* lens, int batch, int upb, int tcap,
                               const Stream& st, long long x) {
+  if (batch <= 64) return uniform_unit(stream_locate_wave(sm, upb, st, x));
   int b0, b1;
   seq_block(batch, b0, b1);
   long long s = sm.tok[threadIdx.x];
@@ -142,24 +247,24 @@ __device__ Unit stream_locate(ScanSmem& sm, const int32_t* lens, int batch, int 
     const int t = clamp_len(lens, b, tcap);
     if (t > 0 && x >= s && x < s + (long long)t * upb) {   // x lies in sequence b
       const int j = (int)((x - s) / t);
-      for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * t, t, st.q);
+      for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * t, t, st);
       sm.found = Unit{b, j, t, base, s + (long long)j * t};
       break;
     }
-    for (int jj = 0; jj < upb; ++jj) base += unit_segments(s + (long long)jj * t, t, st.q);
+    for (int jj = 0; jj < upb; ++jj) base += unit_segments(s + (long long)jj * t, t, st);
     s += (long long)t * upb;
   }
   __syncthreads();
   const Unit u = sm.found;
   __syncthreads();
-  return u;
+  return uniform_unit(u);
 }
 
 // The next non-empty unit after u (the caller knows one exists).
 __device__ __forceinline__ Unit stream_next(const Unit& u, const int32_t* lens, int upb, int tcap,
-                                            long long q) {
+                                            const Stream& st) {
   Unit n = u;
-  n.base = u.base + unit_segments(u.s, u.t, q);
+  n.base = u.base + unit_segments(u.s, u.t, st);
   n.s = u.s + u.t;
   if (u.j + 1 < upb) {
     n.j = u.j + 1;
@@ -169,7 +274,7 @@ __device__ __forceinline__ Unit stream_next(const Unit& u, const int32_t* lens, 
   n.b = u.b + 1;
   n.t = clamp_len(lens, n.b, tcap);
   while (n.t == 0) n.t = clamp_len(lens, ++n.b, tcap);
-  return n;
+  return uniform_unit(n);
 }
 
 // Records where the merge finds a unit's partials (written by the
@@ -473,8 +578,8 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
 
       // Combine the four wavefronts' softmax states through LDS, one block
       // of 16 heads at a time.
-      const int nseg = unit_segments(u.s, u.t, st.q);
-      const int kseg = (int)(r - u.s / st.q);
+      const int nseg = unit_segments(u.s, u.t, st);
+      const int kseg = (int)(r - range_div(u.s, st));
       const size_t slot = (size_t)u.base + kseg;
 #pragma unroll
       for (int bk = 0; bk < HB; ++bk) {
@@ -519,7 +624,7 @@ void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kc
       lo += nt;
       if (lo >= hi) break;
       __syncthreads();   // the combine buffers are read before the next segment's tiles
-      u = stream_next(u, lens, upb, tcap, st.q);
+      u = stream_next(u, lens, upb, tcap, st);
     }
     __syncthreads();
   }
@@ -612,8 +717,8 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
           wave_sync();
         }
       }
-      const int nseg = unit_segments(u.s, u.t, st.q);
-      const int kseg = (int)(r - u.s / st.q);
+      const int nseg = unit_segments(u.s, u.t, st);
+      const int kseg = (int)(r - range_div(u.s, st));
       const size_t slot = (size_t)u.base + kseg;
 #pragma unroll
       for (int s = 0; s < kF32HeadsPerWave; ++s) {
@@ -632,7 +737,7 @@ void decode_split_f32(const float* __restrict__ q, const float* __restrict__ kc,
       publish_unit(unit_info, u, upb, nseg, kseg);
       lo += nt;
       if (lo >= hi) break;
-      u = stream_next(u, lens, upb, tcap, st.q);
+      u = stream_next(u, lens, upb, tcap, st);
       __syncthreads();   // qs is rewritten for the next unit
     }
     __syncthreads();
