@@ -73,6 +73,18 @@ __device__ __forceinline__ long long range_div(long long x, const Stream& st) {
   return d;
 }
 
+// floor(a / b) for a >= 0, b >= 1 through a double quotient, instead of the
+// long sequence of a 64-bit integer division.  The quotients taken here are
+// below 2^45 (W < 2^54 by the plan's bounds, divided by 512 workgroups when
+// W is large; range counts below 2^27; unit indices), so the double quotient
+// is within one of the true one and the remainder fixes it.
+__device__ __forceinline__ long long floor_div(long long a, long long b) {
+  long long d = (long long)((double)a / (double)b);
+  const long long r = a - d * b;
+  d += (r >= b) - (r < 0);
+  return d;
+}
+
 // Segments of a unit occupying stream positions [s, s + t).
 __device__ __forceinline__ int unit_segments(long long s, int t, const Stream& st) {
   return t == 0 ? 0 : (int)(range_div(s + t - 1, st) - range_div(s, st) + 1);
@@ -92,6 +104,7 @@ struct ScanSmem {
   long long tok[kThreads];   // per-thread token base
   int seg[kThreads];         // per-thread segment base
   Unit found;
+  int per_unit;              // segments of every unit when all lengths are equal and Q divides them, else 0
 };
 
 // Block-wide exclusive scan of one value per thread; returns the total.
@@ -177,18 +190,30 @@ __device__ Stream stream_setup_wave(ScanSmem& sm, const int32_t* lens, int batch
   if (q_fixed > 0) {
     st.q = q_fixed;
   } else {
-    st.q = (st.w + gridDim.x - 1) / gridDim.x;
+    st.q = floor_div(st.w + gridDim.x - 1, gridDim.x);
     if (st.q < kMinRange) st.q = kMinRange;
   }
-  st.ranges = (st.w + st.q - 1) / st.q;
+  st.ranges = floor_div(st.w + st.q - 1, st.q);
   st.qinv = 1.0 / (double)st.q;
+  // Equal lengths T that Q divides (the usual case of a batch decoded in
+  // step): every unit starts on a range boundary and holds T / Q segments,
+  // so the slot bases follow without dividing per unit.
+  const int t_first = __builtin_amdgcn_readfirstlane(t);
+  const bool equal = __builtin_amdgcn_ballot_w64(lane < batch && t != t_first) == 0 && t_first > 0;
+  const long long per = equal ? range_div(t_first, st) : 0;
+  sm.tok[lane] = incl - span;
+  sm.tok[64 + lane] = t;
+  if (equal && per * st.q == t_first) {
+    sm.seg[lane] = lane * upb * (int)per;
+    if (lane == 0) sm.per_unit = (int)per;
+    return st;
+  }
   long long s = incl - span;
   int segs = 0;
   for (int j = 0; j < upb; ++j, s += t) segs += unit_segments(s, t, st);
   const int sincl = wave_inclusive_scan(segs);
-  sm.tok[lane] = incl - span;
-  sm.tok[64 + lane] = t;
   sm.seg[lane] = sincl - segs;
+  if (lane == 0) sm.per_unit = 0;
   return st;
 }
 
@@ -202,8 +227,12 @@ __device__ Unit stream_locate_wave(ScanSmem& sm, int upb, const Stream& st, long
   const long long s = readlane64(s_b, l);
   const int tb = __builtin_amdgcn_readlane(t, l);
   int base = __builtin_amdgcn_readlane(base_b, l);
-  const int j = (int)((x - s) / tb);
-  for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * tb, tb, st);
+  const int j = (int)floor_div(x - s, tb);
+  const int per = __builtin_amdgcn_readfirstlane(sm.per_unit);
+  if (per > 0)
+    base += j * per;
+  else
+    for (int jj = 0; jj < j; ++jj) base += unit_segments(s + (long long)jj * tb, tb, st);
   return Unit{l, j, tb, base, s + (long long)j * tb};
 }
 

@@ -131,21 +131,25 @@ def test_backward_nonpositive_scale(scale):
     assert max(errs) <= TOL_REL
 
 
-def test_prefill_4k_backward_full_size_two_groups():
+@pytest.mark.parametrize("quarter", range(4))
+def test_prefill_4k_backward_full_size(quarter):
     """The full prefill-4k workload (B=2, Hq=32, Hkv=8, N=4096, d=128) in the
-    bench's launch configuration; the oracle differentiates two whole KV-head
-    groups (all 4096 rows of 4 query heads each)."""
+    bench's launch configuration; the oracle differentiates every KV-head
+    group (all 4096 rows of its 4 query heads, and the group's dk and dv),
+    four of the sixteen (sequence, KV head) groups per test."""
     need_gpu()
     cfg = gi.CONFIGS["prefill-4k"]
     p = gi.make_prefill(cfg)
     do = gi.make_dout(cfg)
-    say("prefill-4k backward", gi.describe(cfg))
+    say("prefill-4k backward", gi.describe(cfg), "quarter", quarter)
     dq, dk, dv = run_backward(p, do)
     for x in (dq, dk, dv):
         assert np.all(np.isfinite(x))
     g = cfg.num_q_heads // cfg.num_kv_heads
+    groups = [(b, j) for b in range(cfg.batch) for j in range(cfg.num_kv_heads)]
+    per = len(groups) // 4
     worst = 0.0
-    for b, j in ((0, 0), (1, 7)):
+    for b, j in groups[quarter * per:(quarter + 1) * per]:
         rq, rk, rv = oracle.prefill_causal_backward_group(
             gi.to_f64(p.q[b], "bf16"), gi.to_f64(p.k[b], "bf16"), gi.to_f64(p.v[b], "bf16"),
             gi.to_f64(do[b], "bf16"), j, cfg.scale)

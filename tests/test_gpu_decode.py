@@ -72,6 +72,16 @@ SMALL_CASES = [
     ("f32", 2, 8, 2, 64, [1, 300], 320, 64),
     ("f32", 2, 12, 3, 128, [129, 64], 192, 128),
     ("f32", 1, 20, 1, 64, [100], 128, 0),               # fp32, 20 heads on one (two head blocks)
+    # equal lengths, range size left to the device; where the range size
+    # divides the length, slot bases come from the closed form
+    ("bf16", 4, 8, 2, 128, [1024] * 4, 1024, 0),        # closed form: 4 segments per unit
+    ("bf16", 2, 8, 2, 128, [512, 512], 640, 0),         # closed form, padding past T
+    ("bf16", 3, 32, 1, 64, [768] * 3, 768, 0),          # closed form, group 32 (two blocks per unit)
+    ("bf16", 4, 8, 2, 128, [1000] * 4, 1024, 0),        # 256 does not divide 1000: stream scan
+    ("bf16", 2, 8, 2, 128, [200, 200], 256, 0),         # shorter than one range: direct output, no merge
+    ("bf16", 70, 8, 1, 64, [300] * 70, 320, 0),         # more than 64 sequences (block-wide scan)
+    ("bf16", 40, 32, 16, 64, [256] * 40, 256, 0),       # 640 units on 512 workgroups: some take two
+    ("bf16", 2, 64, 2, 128, [1500, 1500], 1536, 0),     # group 32, stream scan
     # many segments per unit: the merge takes several rounds of eight rows per thread
     ("bf16", 1, 8, 2, 64, [5000], 5120, 32),            # 157 segments, 128 per round at d = 64
     ("bf16", 1, 8, 2, 128, [4500], 4608, 32),           # 141 segments, 64 per round at d = 128
