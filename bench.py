@@ -18,7 +18,7 @@ kernels run on (torch's current stream, which the binding launches on).
   python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|
                   paged-llama3-8b|paged-wide-group|fp8-llama3-8b|fp8-wide-group|fp8-mqa-128k|
                   mla-decode]
-                  [--page-size P] [--no-cpu-baseline]
+                  [--page-size P] [--no-cpu-baseline] [--expanded]
 """
 from __future__ import annotations
 
@@ -356,6 +356,46 @@ def bench_wide(args, torch, gi, gqa) -> dict:
     return result
 
 
+def expanded_ab(args, torch, gi, gqa, q, ks, vs, lens, grouped_out, cfg, inp, grouped_ms):
+    """The same decode kernel on an explicitly repeated cache: K and V
+    repeated along the head axis (head h holds KV head h // g, the order of
+    the oracle's repeat) and decoded with Hkv = Hq, each query head reading
+    its own copy.  The result is the same attention; the step reads g times
+    the bytes (study.greatitself.com, "Grouped-Query and Multi-Query
+    Attention", section "Share keys and values without confusing query-head
+    identity": expanding K/V keeps the arithmetic but loses the bandwidth
+    advantage)."""
+    B, Hq, Hkv, d = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    g = Hq // Hkv
+    kx = [torch.repeat_interleave(k, g, dim=1).contiguous() for k in ks]
+    vx = [torch.repeat_interleave(v, g, dim=1).contiguous() for v in vs]
+    rot = len(kx)
+    T = kx[0].shape[2]
+    plan = gqa.gqa_decode_plan(B, Hq, Hq, d, T, gqa.GQA_BF16, 0)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    xout = torch.empty_like(grouped_out)
+
+    def xstep(i):
+        gqa.gqa_decode(q, kx[i % rot], vx[i % rot], lens, scale=cfg.scale, out=xout, workspace=ws)
+
+    for i in range(max(3, args.warmup // 2)):
+        xstep(i)
+    ms = event_time_ms(xstep, args.steps, torch)
+    # both outputs from the same cache copy
+    gqa.gqa_decode(q, ks[0], vs[0], lens, scale=cfg.scale, out=grouped_out)
+    xstep(0)
+    torch.cuda.synchronize()
+    diff = float((xout - grouped_out).abs().max().item())
+    xbytes = decode_kv_bytes(inp.seq_lens, Hq, d, 2)
+    return {"workload": f"{gi.describe(cfg)}: K/V repeated to {Hq} KV heads, same kernel",
+            "kv_bytes": xbytes, "ms_per_step": round(ms, 5),
+            "kv_read_gb_per_s": round(xbytes / (ms * 1e-3) / 1e9, 2),
+            "decode_tokens_per_s": round(B / (ms * 1e-3), 1),
+            "grouped_ms_per_step": round(grouped_ms, 5),
+            "slowdown_vs_grouped": round(ms / grouped_ms, 3),
+            "max_abs_diff_vs_grouped": diff}
+
+
 def cpu_baseline_wide(inp, budget_s: float, max_passes: int = 4):
     """The float64 oracle (oracle.decode_wide) on the host, one sequence per
     call, cycling over the batch until about `budget_s` seconds are spent."""
@@ -397,6 +437,9 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--expanded", action="store_true",
+                    help="also run the same decode kernel on an explicitly repeated cache (Hkv = Hq) "
+                         "and report it beside the grouped step in \"expanded_ab\"")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 256 MiB device copy kernel (counter calibration)")
@@ -539,6 +582,9 @@ def main():
                      "ms_per_launch": round(ms_split, 5)},
         "timed_wall_s": round(wall, 4),
     }
+
+    if args.expanded and cfg.dtype == "bf16" and not (paged or fp8) and Hq > Hkv:
+        result["expanded_ab"] = expanded_ab(args, torch, gi, gqa, q, ks, vs, lens, out, cfg, inp, ms_step)
 
     if not args.no_prefill:
         pc = gi.CONFIGS["prefill-4k"]

@@ -53,3 +53,17 @@ def test_more_than_one_gpu_exits_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"], capture_output=True,
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_expanded_cache_ab_line():
+    """--expanded: the same decode kernel on K/V repeated to Hq heads gives the
+    same attention (within the bf16 tolerance of the grouped result) and
+    reads g = 4 times the bytes, so its step is several times longer."""
+    need_gpu()
+    d = run_bench("--steps", "4", "--warmup", "1", "--no-cpu-baseline", "--no-prefill", "--expanded")
+    x = d["expanded_ab"]
+    say("expanded", x)
+    assert x["max_abs_diff_vs_grouped"] <= 2e-2
+    assert x["kv_bytes"] == 4 * 1073741824
+    assert x["slowdown_vs_grouped"] > 2.0
+    assert x["ms_per_step"] > 0 and x["grouped_ms_per_step"] == d["ms_per_step"]
