@@ -225,3 +225,25 @@ def test_decode_matches_prefill_last_row():
     dec = gqa.gqa_decode(q[:, :, -1].contiguous(), k, v, lens)
     torch.cuda.synchronize()
     assert max_err(dec.cpu().numpy(), pre[:, :, -1].cpu().numpy().astype(np.float64)) <= 2e-2
+
+
+def test_decode_at_largest_cache_capacity():
+    """The largest cache the plan accepts at d = 128: 4,194,303 tokens per
+    (sequence, KV head), the limit of one head's 32-bit byte offsets
+    (T * d * 4 < 2^31).  Three sequences put the third one's rows more than
+    2^31 bytes past the cache's base, so element offsets must be 64-bit; the
+    lengths sit at and just below the capacity (the tail past each length is
+    NaN), and each unit is split into hundreds of segments, which the merge
+    combines in several rounds."""
+    need_gpu()
+    T = (2 ** 31 - 1) // (128 * 4)
+    lens = [T, T - 1, T - 37]
+    inp = gi.small_decode("bf16", 3, 1, 1, 128, lens, T, seed=4242)
+    say("largest cache", T, "tokens x 3 sequences")
+    got = run_decode(inp)
+    for b in range(3):
+        ref, _ = oracle.decode_one(gi.to_f64(inp.q[b, 0], "bf16"), gi.to_f64(inp.k_cache[b, :, :lens[b]], "bf16"),
+                                   gi.to_f64(inp.v_cache[b, :, :lens[b]], "bf16"), lens[b], 0, 1, inp.cfg.scale)
+        err = max_err(got[b, 0], ref)
+        say("sequence", b, "max err", err)
+        assert err <= TOL["bf16"]

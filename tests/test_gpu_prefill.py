@@ -128,3 +128,26 @@ def test_large_scale_moves_reference_often():
     err, lerr = max_err(out.cpu().numpy(), ref), max_err(lse.cpu().numpy(), ref_lse)
     say("scale 1 max err", err, "lse err", lerr)
     assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
+
+
+def test_prefill_long_prompt_sampled_rows():
+    """A 131,072-token causal prefill (B=1, Hq=4, Hkv=1, d=128; 4,096 q-tiles
+    of one KV head): rows at tile and q-tile boundaries, the last rows and
+    random rows of every head against the oracle's rows (row i attends keys
+    0..i), output and lse."""
+    need_gpu()
+    N = 131072
+    p = gi.small_prefill(1, 4, 1, N, 128, seed=5151)
+    say("prefill long prompt", N)
+    out, lse = run_prefill(p)
+    rng = np.random.default_rng(7)
+    rows = sorted({0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 4095, 4096, 65535, 65536, N - 65, N - 64, N - 2, N - 1}
+                  | set(int(r) for r in rng.integers(0, N, size=14)))
+    k64, v64 = gi.to_f64(p.k[0], "bf16"), gi.to_f64(p.v[0], "bf16")
+    worst = 0.0
+    for h in range(4):
+        ref, ref_lse = oracle.prefill_causal_rows(gi.to_f64(p.q[0, h, rows], "bf16"), k64, v64, rows, h, 4,
+                                                  p.cfg.scale)
+        worst = max(worst, max_err(out[0, h, rows], ref), max_err(lse[0, h, rows], ref_lse))
+    say("max err over", len(rows), "rows x 4 heads", worst)
+    assert worst <= TOL["bf16"]
