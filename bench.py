@@ -15,7 +15,7 @@ timed region and rotated over several copies so the 256 MB MALL cannot serve
 repeated steps.  Kernel durations come from HIP events on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
-  python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|
+  python bench.py [--steps K] [--warmup W] [--workload llama3-8b|wide-group|mqa-128k|group-32|group-71|
                   paged-llama3-8b|paged-wide-group|fp8-llama3-8b|fp8-wide-group|fp8-mqa-128k|
                   mla-decode]
                   [--page-size P] [--no-cpu-baseline] [--expanded]
@@ -427,7 +427,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b",
-                    choices=["llama3-8b", "wide-group", "mqa-128k", "paged-llama3-8b", "paged-wide-group",
+                    choices=["llama3-8b", "wide-group", "mqa-128k", "group-32", "group-71", "paged-llama3-8b", "paged-wide-group",
                              "fp8-llama3-8b", "fp8-wide-group", "fp8-mqa-128k", "mla-decode"])
     ap.add_argument("--page-size", type=int, default=16, help="tokens per page for the paged-* workloads")
     ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -16,6 +16,9 @@ Workloads (the five shapes the library is measured and checked on):
   mla-decode  (WIDE_CONFIGS) decode in the absorbed-MLA shape, bf16: B=64,
       Hq=128 query heads over one cached 576-column row per token (512 latent
       + 64 rotary), value = the first 512 columns, 4096 tokens, seed 1006
+  group-32    32 query heads on one KV head, bf16: B=32, d=128, 8192 tokens, seed 1007
+  group-71    71 query heads on one KV head (the Falcon-7B head count), bf16:
+      B=16, d=64, 8192 tokens, seed 1008
 
 Recipe: seeds 1001..1005 in the order listed above; ``SeedSequence(seed).spawn(4)`` gives
 independent PCG64 streams for (lengths, Q, K, V) in that order; values are
@@ -85,6 +88,9 @@ CONFIGS = {
     "wide-group": DecodeConfig("wide-group-ragged-decode-bf16", "bf16", 64, 32, 2, 128, 32768, 1024, 32768, 1003),
     "mqa-128k": DecodeConfig("mqa-long-decode-bf16", "bf16", 4, 16, 1, 128, 131072, 131072, 131072, 1004),
     "prefill-4k": PrefillConfig("causal-prefill-bf16", "bf16", 2, 32, 8, 128, 4096, 1005),
+    # groups wider than one 16-head block (traffic of the shared K/V read)
+    "group-32": DecodeConfig("group-32-decode-bf16", "bf16", 32, 32, 1, 128, 8192, 8192, 8192, 1007),
+    "group-71": DecodeConfig("group-71-decode-bf16", "bf16", 16, 71, 1, 64, 8192, 8192, 8192, 1008),
 }
 
 
