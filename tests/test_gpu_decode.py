@@ -247,3 +247,41 @@ def test_decode_at_largest_cache_capacity():
         err = max_err(got[b, 0], ref)
         say("sequence", b, "max err", err)
         assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(3, 8, 2, 128), (2, 16, 1, 128), (2, 64, 2, 128), (2, 12, 3, 64)],
+                         ids=lambda s: "B{}-{}on{}-d{}".format(*s))
+def test_single_token_is_v0_bit_exact(shape):
+    """A sequence holding one token: its only weight is 2^0 = 1 and the sum is
+    1, so every query head of the group returns that token's V row exactly
+    (the one-segment path writes it straight to the output); longer
+    sequences in the same batch keep the tolerance."""
+    need_gpu()
+    B, Hq, Hkv, d = shape
+    lens = [1] + [97 * (i + 1) for i in range(B - 1)]
+    inp = gi.small_decode("bf16", B, Hq, Hkv, d, lens, 512, seed=zlib.crc32(repr(shape).encode()) % 100000)
+    say("single token", shape, lens)
+    got = run_decode(inp)
+    g = Hq // Hkv
+    for h in range(Hq):
+        assert np.array_equal(got[0, h], gi.bf16_bits_to_f32(inp.v_cache[0, h // g, 0]))
+    assert max_err(got, oracle_full(inp)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_zero_scale_gives_mean_of_v(split):
+    """scale = 0: every attended token has weight 1, so each head returns the
+    mean of its KV head's V rows over the sequence (a closed form that does
+    not go through the oracle's softmax)."""
+    need_gpu()
+    lens = [1, 300, 1000]
+    inp = gi.small_decode("bf16", 3, 16, 2, 128, lens, 1024, seed=777)
+    q, k, v, sl = decode_tensors(inp)
+    out = gqa.gqa_decode(q, k, v, sl, scale=0.0, split_tokens=split)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    vf = gi.to_f64(inp.v_cache, "bf16")
+    for b, t in enumerate(lens):
+        for h in range(16):
+            mean = vf[b, h // 8, :t].mean(axis=0)
+            assert np.max(np.abs(got[b, h] - mean)) <= 1e-3, (b, h)
