@@ -285,3 +285,52 @@ def test_zero_scale_gives_mean_of_v(split):
         for h in range(16):
             mean = vf[b, h // 8, :t].mean(axis=0)
             assert np.max(np.abs(got[b, h] - mean)) <= 1e-3, (b, h)
+
+
+def graph_replays_match_eager(step, out_graph, out_eager, disturb, replays=3):
+    """Capture `step` (which writes out_graph) in a HIP graph and replay it:
+    before each replay out_graph is NaN-filled outside the graph, after it the
+    program's own eager work (`disturb`, which reuses the same workspace)
+    runs with a synchronisation between, and every replay must equal the
+    eager result bit for bit."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(replays):
+        out_graph.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_graph, out_eager), f"replay {r}"
+        disturb()
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_decode_step_replays_from_a_hip_graph(split):
+    """The decode step (split kernel and merge) launched with a caller-owned
+    workspace can be captured in a HIP graph: the C call allocates nothing
+    and records no memset, and the kernels rewrite every workspace byte they
+    read, so replays after eager calls on other inputs are exact."""
+    need_gpu()
+    inp = gi.small_decode("bf16", 4, 32, 8, 128, [3000, 17, 4096, 1], 4096, seed=2929)
+    q, k, v, lens = decode_tensors(inp)
+    plan = gqa.gqa_decode_plan(4, 32, 8, 128, 4096, gqa.GQA_BF16, split)
+    ws = gqa.decode_workspace(plan.workspace_bytes)
+    say("graph replay, split", split, "workspace bytes", plan.workspace_bytes)
+    out_e = gqa.gqa_decode(q, k, v, lens, scale=inp.cfg.scale, workspace=ws, split_tokens=split)
+    torch.cuda.synchronize()
+    assert max_err(out_e.cpu().numpy(), oracle_full(inp)) <= TOL["bf16"]
+    out_g = torch.empty_like(out_e)
+    out_x = torch.empty_like(out_e)
+    graph_replays_match_eager(
+        lambda: gqa.gqa_decode(q, k, v, lens, scale=inp.cfg.scale, out=out_g, workspace=ws, split_tokens=split),
+        out_g, out_e,
+        lambda: gqa.gqa_decode(q * 3, k, v, lens.flip(0).contiguous(), scale=inp.cfg.scale, out=out_x,
+                               workspace=ws, split_tokens=split))

@@ -74,3 +74,38 @@ def test_noalloc_repeated_call_is_bitwise_stable():
     a = noalloc(inp)
     b = noalloc(inp)
     assert np.array_equal(a, b)
+
+
+def test_noalloc_step_replays_from_a_hip_graph():
+    """The caller this entry point is for: code under HIP graph capture.  One
+    decode step through gqa_decode_noalloc is captured and replayed three
+    times, with eager calls on other inputs (which rewrite the same scratch)
+    and synchronisations between; every replay equals the eager call bit for
+    bit, and the eager call matches the oracle."""
+    need_gpu()
+    inp = gi.small_decode("bf16", 3, 16, 2, 128, [2500, 1, 900], 2560, seed=4300)
+    q, k, v, lens = decode_tensors(inp)
+    say("noalloc graph replay", q.shape, inp.seq_lens.tolist())
+    out_e = torch.empty((3, 16, 128), dtype=torch.float32, device="cuda")
+    gqa.gqa_decode_noalloc(q, k, v, lens, out_e, scale=inp.cfg.scale)
+    torch.cuda.synchronize()
+    assert max_err(out_e.cpu().numpy(), reference(inp)) <= TOL["bf16"]
+    out_g = torch.empty_like(out_e)
+    out_x = torch.empty_like(out_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gqa.gqa_decode_noalloc(q, k, v, lens, out_g, scale=inp.cfg.scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gqa.gqa_decode_noalloc(q, k, v, lens, out_g, scale=inp.cfg.scale)
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {r}"
+        gqa.gqa_decode_noalloc(q * 3, k, v, lens.flip(0).contiguous(), out_x, scale=inp.cfg.scale)
+        torch.cuda.synchronize()
