@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -51,9 +52,12 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t tca
   if ((int64_t)tcap * d * 4 > INT32_MAX) return GQA_ERR_SHAPE;
   const int64_t g = hq / hkv;
   const int64_t nhb = (g + gqa::kDecodeHeadBlock - 1) / gqa::kDecodeHeadBlock;
-  // bf16 and E4M3 caches put two head blocks in one unit when the group has
-  // more than one block (one pass over the KV head for up to 32 heads)
-  const int hbu = (dtype != GQA_F32 && nhb > 1) ? 2 : 1;
+  // bf16 and E4M3 caches put several head blocks in one unit when the group
+  // has more than one block: two at head_dim 128 (one pass over the KV head
+  // for up to 32 heads), up to five at head_dim 64 (up to 80 heads)
+  const int hbu = (dtype == GQA_F32 || nhb == 1)
+                      ? 1
+                      : (d == 64 ? (int)std::min<int64_t>(nhb, gqa::kMaxHeadBlocks64) : 2);
   const int64_t nhg = (nhb + hbu - 1) / hbu;
   const int64_t units = (int64_t)batch * hkv * nhg;
   const int64_t work = units * (int64_t)tcap;   // upper bound on token-units

@@ -11,11 +11,13 @@
 // query heads act as extra query rows against the shared K/V).
 //
 // Work partition (balanced "stream" split).  A unit is one (sequence, KV
-// head, block of 16 query heads, or two blocks for bf16 and E4M3 caches
-// when the group is wider); its work is the sequence's T_b cached tokens.  The units' tokens are laid end to end into one stream of W
-// token-units, and range r of the stream is [r*Q, (r+1)*Q): every range has
-// the same size no matter how ragged the lengths are, and about one range
-// runs per resident workgroup, so no workgroup idles at the tail.  Q is
+// head, block of 16 query heads, or for bf16 and E4M3 caches when the group
+// is wider, two blocks at head_dim 128 and up to five at head_dim 64); its
+// work is the sequence's T_b cached tokens.  The units' tokens are laid end
+// to end into one stream of W token-units, and range r of the stream is
+// [r*Q, (r+1)*Q): every range has the same size no matter how ragged the
+// lengths are, and about one range runs per resident workgroup, so no
+// workgroup idles at the tail.  Q is
 // chosen on the device from the actual lengths (Q = ceil(W / workgroups),
 // at least kMinRange) unless the caller fixes it.  The piece of a range that
 // falls inside one unit is a segment; a unit split over n > 1 segments gets
@@ -443,10 +445,11 @@ __device__ __forceinline__ void load_tile_f8(DecodeTileF8<D>& t, __amdgpu_buffer
 // kPaged: K/V in a page pool addressed through a block table.  kFp8: K/V
 // stored as E4M3 codes with one float scale per KV head (k_scale folds into
 // the softmax scale, v_scale multiplies the normalised output).  HB: 16-head
-// blocks per unit; with HB = 2 a unit covers 32 query heads of one KV head,
-// both blocks scored from the same K registers and accumulated from the same
-// V tile, so a group of up to 32 heads reads its K/V once (two waves per
-// SIMD, as launched, leave a wavefront 256 registers for the second block).
+// blocks per unit; with HB > 1 a unit covers 16 * HB query heads of one KV
+// head, every block scored from the same K registers and accumulated from
+// the same V tile, so the group reads its K/V once (two waves per SIMD, as
+// launched, leave a wavefront 256 registers: room for the accumulators and
+// query operands of two blocks at head_dim 128, of five at head_dim 64).
 template <int D, bool kPaged, bool kFp8, int HB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HB == 1 ? GQA_DECODE_WAVES_PER_EU : 2)))
 void decode_split_bf16(const __bf16* __restrict__ q, const void* __restrict__ kcv,
@@ -905,16 +908,27 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, cons
   } else {                           \
     GQA_SPLIT2(DD, PG, F8, 1);       \
   }
+#define GQA_SPLIT64(PG, F8)          \
+  if (s.hb == 5) {                   \
+    GQA_SPLIT2(64, PG, F8, 5);       \
+  } else if (s.hb == 4) {            \
+    GQA_SPLIT2(64, PG, F8, 4);       \
+  } else if (s.hb == 3) {            \
+    GQA_SPLIT2(64, PG, F8, 3);       \
+  } else {                           \
+    GQA_SPLIT(64, PG, F8)            \
+  }
     if (s.dtype == 2) {
       if (s.d == 128) { GQA_SPLIT(128, false, true) }
-      else { GQA_SPLIT(64, false, true) }
+      else { GQA_SPLIT64(false, true) }
     } else if (paged.table != nullptr) {
       if (s.d == 128) { GQA_SPLIT(128, true, false) }
-      else { GQA_SPLIT(64, true, false) }
+      else { GQA_SPLIT64(true, false) }
     } else {
       if (s.d == 128) { GQA_SPLIT(128, false, false) }
-      else { GQA_SPLIT(64, false, false) }
+      else { GQA_SPLIT64(false, false) }
     }
+#undef GQA_SPLIT64
 #undef GQA_SPLIT
 #undef GQA_SPLIT2
   } else {

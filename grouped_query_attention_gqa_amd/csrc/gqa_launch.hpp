@@ -7,10 +7,13 @@
 namespace gqa {
 
 // Query heads of one MFMA column block in decode.  A decode unit covers one
-// block, or two (32 heads) for bf16 and E4M3 caches when the group is larger
-// than 16, so groups of up to 32 query heads share a single pass over their
-// KV head.
+// block, or, for bf16 and E4M3 caches when the group is larger than 16, two
+// blocks (32 heads) at head_dim 128 and up to kMaxHeadBlocks64 blocks (80
+// heads) at head_dim 64, whose accumulators take half the registers; so
+// groups of up to 32 (head_dim 128) or 80 (head_dim 64) query heads share a
+// single pass over their KV head.
 constexpr int kDecodeHeadBlock = 16;
+constexpr int kMaxHeadBlocks64 = 5;
 // Decode: tokens per wavefront iteration (bf16 path) and waves per workgroup.
 constexpr int kDecodeWaveTile = 32;
 constexpr int kDecodeWaves = 4;
@@ -26,7 +29,8 @@ constexpr int kPersistentWorkgroups = GQA_DECODE_GRID;
 
 struct DecodeShape {
   int batch, hq, hkv, d, tcap;
-  int hb;            // 16-head blocks per unit: 2 for bf16 and E4M3 caches when g > 16, else 1
+  int hb;            // 16-head blocks per unit: 1 for fp32 caches or g <= 16, else 2 at d = 128
+                     // and min(ceil(g / 16), kMaxHeadBlocks64) at d = 64
   int nhg;           // units per KV head: ceil(ceil(g / 16) / hb)
   int units;         // batch * hkv * nhg
   int q_fixed;       // tokens per range fixed by the caller, 0 = chosen on the device

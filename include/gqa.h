@@ -79,8 +79,9 @@ const char* gqa_last_hip_error(void);
 
 /*
  * Launch plan of a decode call.  Decode lays the cached tokens of every
- * (sequence, KV head, block of up to 16 query heads; up to 32 for bf16 and
- * E4M3 caches when the group has more than 16) end to end into one
+ * (sequence, KV head, block of up to 16 query heads; for bf16 and E4M3
+ * caches when the group has more than 16, up to 32 at head_dim 128 and up
+ * to 80 at head_dim 64) end to end into one
  * stream and cuts it into equal ranges, one per workgroup, so ragged batches
  * stay balanced; a range's piece inside one sequence is attended by one
  * workgroup for all query heads of the group, and a sequence that spans

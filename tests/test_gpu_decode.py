@@ -68,6 +68,12 @@ SMALL_CASES = [
     ("bf16", 1, 48, 1, 128, [2000], 2048, 0),           # group 48: a two-block unit and a one-block unit
     ("bf16", 2, 128, 2, 128, [3000, 64], 3072, 0),      # group 64: two units of two blocks per KV head
     ("bf16", 2, 32, 2, 128, [4096, 1500], 4096, 0),     # group 16, wide
+    # head_dim 64: up to five blocks (80 heads) share one unit
+    ("bf16", 1, 71, 1, 64, [300], 320, 64),             # 71 heads: five blocks in one unit
+    ("bf16", 2, 48, 1, 64, [1000, 77], 1024, 0),        # three blocks
+    ("bf16", 2, 128, 2, 64, [700, 1300], 1344, 0),      # group 64 on two KV heads: four blocks
+    ("bf16", 1, 96, 1, 64, [1500], 1536, 0),            # group 96: a five-block and a one-block unit
+    ("bf16", 2, 80, 1, 64, [2048, 2048], 2048, 0),      # five full blocks, closed-form slot bases
     ("bf16", 3, 6, 2, 64, [0, 5, 64], 64, 0),           # empty sequence
     ("f32", 2, 8, 2, 64, [1, 300], 320, 64),
     ("f32", 2, 12, 3, 128, [129, 64], 192, 128),
@@ -163,11 +169,10 @@ def test_mqa_128k_decode_full():
     assert err <= TOL["bf16"]
 
 
-def _mapping_probe(B, Hq, Hkv, T, split):
+def _mapping_probe(B, Hq, Hkv, T, split, d=128):
     """K = 0 and V constant per (b, KV head): V[...,0] = kv head, V[...,1] = b,
     V[...,2] = 1.  Every weight is exactly 1, so out[b,h,0] = h // g and
     out[b,h,1] = b exactly (sums stay below 2^24)."""
-    d = 128
     k = torch.zeros(B, Hkv, T, d, dtype=torch.bfloat16, device="cuda")
     v = torch.zeros(B, Hkv, T, d, dtype=torch.float32)
     v[..., 0] = torch.arange(Hkv, dtype=torch.float32)[None, :, None]
@@ -181,18 +186,19 @@ def _mapping_probe(B, Hq, Hkv, T, split):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,T", [(32, 32, 8, 8192), (4, 16, 1, 4096), (3, 71, 1, 64), (2, 6, 2, 128),
-                                           (2, 96, 2, 256), (2, 40, 1, 128)])
-def test_mapping_probe_bit_exact(B, Hq, Hkv, T):
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(32, 32, 8, 8192, 128), (4, 16, 1, 4096, 128), (3, 71, 1, 64, 128),
+                                             (2, 6, 2, 128, 128), (2, 96, 2, 256, 128), (2, 40, 1, 128, 128),
+                                             (3, 71, 1, 64, 64), (2, 96, 2, 256, 64), (2, 170, 2, 96, 64)])
+def test_mapping_probe_bit_exact(B, Hq, Hkv, T, d):
     need_gpu()
-    say("mapping probe", B, Hq, Hkv, T)
+    say("mapping probe", B, Hq, Hkv, T, d)
     g = Hq // Hkv
-    out = _mapping_probe(B, Hq, Hkv, T, split=((T + 63) // 64) * 64)   # one split: exact
+    out = _mapping_probe(B, Hq, Hkv, T, split=((T + 63) // 64) * 64, d=d)   # one split: exact
     want_kv = np.array([h // g for h in range(Hq)], dtype=np.float32)
     assert np.array_equal(out[:, :, 0], np.broadcast_to(want_kv, (B, Hq)))
     assert np.array_equal(out[:, :, 1], np.broadcast_to(np.arange(B, dtype=np.float32)[:, None], (B, Hq)))
     assert np.all(out[:, :, 2] == 1.0) and np.all(out[:, :, 3:] == 0.0)
-    multi = _mapping_probe(B, Hq, Hkv, T, split=64)        # merged splits: exact after rounding
+    multi = _mapping_probe(B, Hq, Hkv, T, split=64, d=d)   # merged splits: exact after rounding
     assert np.array_equal(np.rint(multi[:, :, 0]), out[:, :, 0])
     assert np.array_equal(np.rint(multi[:, :, 1]), out[:, :, 1])
 

@@ -49,6 +49,8 @@ CASES = [
     (2, 64, 2, 128, [1500, 40], 1536, 0),     # group 32: two head blocks per unit
     (2, 40, 1, 64, [700, 129], 768, 128),     # group 40: a two-block unit and an 8-head unit
     (2, 12, 3, 64, [33, 250], 256, 0),
+    (1, 71, 1, 64, [900], 1024, 0),           # head_dim 64: 71 heads, five blocks in one unit
+    (2, 64, 1, 64, [500, 333], 512, 64),      # four blocks
 ]
 
 

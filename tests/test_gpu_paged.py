@@ -53,7 +53,9 @@ CASES = [
     (1, 4, 4, 128, [97], 128, 1),          # one token per page
     (2, 12, 3, 64, [33, 250], 256, 8),     # group 4 of 12, pages smaller than a tile
     (2, 64, 2, 128, [1000, 333], 1024, 16),  # group 32: two head blocks per unit
-    (1, 48, 1, 64, [777], 800, 32),        # group 48: a two-block unit and a one-block unit
+    (1, 48, 1, 64, [777], 800, 32),        # group 48 at head_dim 64: three blocks in one unit
+    (2, 71, 1, 64, [600, 129], 640, 16),   # 71 heads at head_dim 64: five blocks in one unit
+    (1, 128, 2, 64, [1000], 1024, 64),     # group 64 at head_dim 64: four blocks
 ]
 
 
