@@ -103,6 +103,26 @@ FP8 = _cache_cases(8, paged=False)
 WIDE = _wide_cases(6)
 
 
+def _many_block_cases(n):
+    """head_dim 64 with groups of 33 to 96 heads: units of three to five
+    16-head blocks (and a second unit past 80 heads)."""
+    cases = []
+    for i in range(n):
+        hkv = int(_rng.choice([1, 2]))
+        g = int(_rng.integers(33, 97))
+        b = int(_rng.integers(1, 5))
+        tcap = int(_rng.integers(1, 3000))
+        lens = _rng.integers(0, tcap + 1, size=b)
+        lens[int(_rng.integers(0, b))] = tcap
+        split = int(_rng.choice([0, 0, 64, 256]))
+        cases.append(("fp8" if i % 4 == 3 else "bf16", b, g * hkv, hkv, tcap, tuple(int(t) for t in lens), split,
+                      bool(i % 2)))
+    return cases
+
+
+MANY_BLOCKS = _many_block_cases(8)
+
+
 def _cache_id(c):
     return "B{}-{}on{}-d{}-T{}-{}".format(*c[:5], c[6])
 
@@ -197,3 +217,19 @@ def test_random_wide_shapes(case):
     for b, t in enumerate(lens):
         if t == 0:
             assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("case", MANY_BLOCKS,
+                         ids=lambda c: "{}-B{}-{}on{}-d64-T{}-split{}-{}".format(*c[:5], c[6], "stages" if c[7] else "call"))
+def test_random_many_block_units(case):
+    need_gpu()
+    kind, B, Hq, Hkv, T, lens, split, stages = case
+    inp = gi.small_decode("bf16", B, Hq, Hkv, 64, list(lens), T, seed=sum(lens) % 9973 + 3 * Hq)
+    say("random many-block", case)
+    if kind == "fp8":
+        fp = gi.make_fp8(inp)
+        err = max_err(run_fp8(fp, split), fp8_oracle(fp))
+    else:
+        err = max_err(run_decode(inp, split_tokens=split, stages=stages), oracle_full(inp))
+    say("max err", err)
+    assert err <= TOL["bf16"]
