@@ -8,7 +8,9 @@ Default workload (one JSON line on stdout):
   value = KV-cache bytes read per step / step time (GB/s).
   The same run also times causal prefill (B=2, Hq=32, Hkv=8, N=4096, d=128)
   and its backward (dq, dk, dv) and reports their TFLOP/s in the "prefill"
-  and "prefill_backward" objects.
+  and "prefill_backward" objects, with the vendor's bf16 GEMM timed beside
+  the prefill as the board's attainable dense-product rate
+  ("prefill.matmul_reference").
 
 Inputs are seeded synthetic N(0,1) values; K/V are resident in HBM before the
 timed region and rotated over several copies so the 256 MB MALL cannot serve
@@ -151,6 +153,30 @@ COUNTED_KERNELS = {   # kernel-name substring -> sources key
     "prefill_bwd_dkdv": "prefill_bwd_dkdv",
     "decode_wide_bf16": "decode_wide",
 }
+
+
+def matmul_reference(torch, iters: int, n: int = 8192) -> dict:
+    """The vendor library's bf16 GEMM on the same GPU in the same run: one
+    n x n x n torch.matmul (hipBLASLt) on contiguous operands, timed like the
+    prefill.  It is the attainable matrix-core rate of a plain dense product
+    on this board, where sustained MFMA load lowers the shader clock below
+    the 2.4 GHz the 2.5 PFLOP/s figure assumes; context for the prefill's
+    fraction, not a peak the roofline uses."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+
+    def mm(i):
+        torch.matmul(a, b, out=c)
+
+    for i in range(5):
+        mm(i)
+    ms = event_time_ms(mm, iters, torch)
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"kernel": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), contiguous operands", "value": round(tf, 2),
+            "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
+            "pct_of_mfma_peak": round(100 * tf / BF16_MFMA_PEAK_TFLOPS, 2)}
 
 
 def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
@@ -613,6 +639,10 @@ def main():
                          "algorithmic_bytes": prefill_bytes(pc.batch, pc.num_q_heads, pc.num_kv_heads,
                                                             pc.seq_len, pc.head_dim)},
         }
+
+        ref = matmul_reference(torch, max(100, args.steps))
+        ref["prefill_over_reference"] = round(tf / ref["value"], 4)
+        result["prefill"]["matmul_reference"] = ref
 
         # backward of the same prefill: dq, dk, dv from (q, k, v, out, lse, dout)
         pdo = torch.from_numpy(gi.make_dout(pc).view(np.int16)).view(torch.bfloat16).cuda()

@@ -47,6 +47,8 @@ def test_default_bench_line():
         p = d[part]
         assert p["value"] > 0 and p["roofline"]["bound"] == bound
         assert 0 < p["roofline"]["frac"] < 1
+    ref = d["prefill"]["matmul_reference"]
+    assert ref["unit"] == "TFLOP/s" and ref["value"] > 0 and ref["prefill_over_reference"] > 0
 
 
 def test_more_than_one_gpu_exits_with_a_message():
