@@ -10,7 +10,8 @@ Default workload (one JSON line on stdout):
   and its backward (dq, dk, dv) and reports their TFLOP/s in the "prefill"
   and "prefill_backward" objects, with the vendor's bf16 GEMM timed beside
   the prefill as the board's attainable dense-product rate
-  ("prefill.matmul_reference").
+  ("prefill.matmul_reference") and torch's own flash attention on the same
+  prefill inputs ("prefill.vendor_attention_reference").
 
 Inputs are seeded synthetic N(0,1) values; K/V are resident in HBM before the
 timed region and rotated over several copies so the 256 MB MALL cannot serve
@@ -177,6 +178,31 @@ def matmul_reference(torch, iters: int, n: int = 8192) -> dict:
     return {"kernel": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), contiguous operands", "value": round(tf, 2),
             "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
             "pct_of_mfma_peak": round(100 * tf / BF16_MFMA_PEAK_TFLOPS, 2)}
+
+
+def vendor_attention_reference(torch, q, k, v, ours, scale: float, iters: int, flops: int) -> dict:
+    """torch's own causal attention on the same prefill inputs, with the
+    flash backend forced (on ROCm an AOTriton kernel; enable_gqa lets it
+    read the grouped K/V in place), timed like the prefill.  Context for the
+    prefill's rate, with the largest difference from this library's output;
+    None in every figure if the backend is not available."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    name = "torch scaled_dot_product_attention, flash backend, is_causal, enable_gqa"
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            def call(i):
+                return F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale, enable_gqa=True)
+
+            o = call(0)
+            torch.cuda.synchronize()
+            diff = float((o.float() - ours).abs().max())
+            ms = event_time_ms(call, iters, torch)
+    except RuntimeError as e:
+        return {"kernel": name, "value": None, "unit": "TFLOP/s", "error": str(e)[:200]}
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": name, "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
+            "max_abs_diff_from_this_library": round(diff, 6)}
 
 
 def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
@@ -643,6 +669,10 @@ def main():
         ref = matmul_reference(torch, max(100, args.steps))
         ref["prefill_over_reference"] = round(tf / ref["value"], 4)
         result["prefill"]["matmul_reference"] = ref
+        att = vendor_attention_reference(torch, pq, pk, pv, pout, pc.scale, max(50, args.steps // 2), fl)
+        if att["value"]:
+            att["prefill_over_reference"] = round(tf / att["value"], 4)
+        result["prefill"]["vendor_attention_reference"] = att
 
         # backward of the same prefill: dq, dk, dv from (q, k, v, out, lse, dout)
         pdo = torch.from_numpy(gi.make_dout(pc).view(np.int16)).view(torch.bfloat16).cuda()

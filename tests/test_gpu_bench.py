@@ -49,6 +49,9 @@ def test_default_bench_line():
         assert 0 < p["roofline"]["frac"] < 1
     ref = d["prefill"]["matmul_reference"]
     assert ref["unit"] == "TFLOP/s" and ref["value"] > 0 and ref["prefill_over_reference"] > 0
+    att = d["prefill"]["vendor_attention_reference"]
+    if att["value"] is not None:   # the same attention within the bf16 tolerance
+        assert att["max_abs_diff_from_this_library"] <= 2e-2
 
 
 def test_more_than_one_gpu_exits_with_a_message():
