@@ -10,8 +10,9 @@ Default workload (one JSON line on stdout):
   and its backward (dq, dk, dv) and reports their TFLOP/s in the "prefill"
   and "prefill_backward" objects, with the vendor's bf16 GEMM timed beside
   the prefill as the board's attainable dense-product rate
-  ("prefill.matmul_reference") and torch's own flash attention on the same
-  prefill inputs ("prefill.vendor_attention_reference").
+  ("prefill.matmul_reference") and torch's own flash attention, forward and
+  backward, on the same prefill inputs ("vendor_attention_reference" in
+  both objects).
 
 Inputs are seeded synthetic N(0,1) values; K/V are resident in HBM before the
 timed region and rotated over several copies so the 256 MB MALL cannot serve
@@ -203,6 +204,36 @@ def vendor_attention_reference(torch, q, k, v, ours, scale: float, iters: int, f
     tf = flops / (ms * 1e-3) / 1e12
     return {"kernel": name, "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
             "max_abs_diff_from_this_library": round(diff, 6)}
+
+
+def vendor_attention_backward_reference(torch, q, k, v, dout, ours, scale: float, iters: int,
+                                        flops: float) -> dict:
+    """The backward of torch's flash-backend causal attention (enable_gqa, so
+    the K/V gradients are summed over each group) on the same inputs and
+    upstream gradient, timed like this library's backward; context, with the
+    largest difference of each gradient from this library's, relative to that
+    gradient's largest magnitude."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    name = "torch scaled_dot_product_attention backward, flash backend, is_causal, enable_gqa"
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            qr, kr, vr = (t.detach().clone().requires_grad_(True) for t in (q, k, v))
+            o = F.scaled_dot_product_attention(qr, kr, vr, is_causal=True, scale=scale, enable_gqa=True)
+
+            def call(i):
+                return torch.autograd.grad(o, (qr, kr, vr), dout, retain_graph=True)
+
+            grads = call(0)
+            torch.cuda.synchronize()
+            rel = max(float((g.float() - r).abs().max() / r.abs().max()) for g, r in zip(grads, ours))
+            del grads
+            ms = event_time_ms(call, iters, torch, min_per_batch=5)
+    except RuntimeError as e:
+        return {"kernel": name, "value": None, "unit": "TFLOP/s", "error": str(e)[:200]}
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": name, "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
+            "max_rel_diff_from_this_library": round(rel, 6)}
 
 
 def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
@@ -710,6 +741,10 @@ def main():
                          "executed_flops": 3.5 * prefill_flops(pc.batch, pc.num_q_heads, pc.seq_len,
                                                                pc.head_dim)},
         }
+        batt = vendor_attention_backward_reference(torch, pq, pk, pv, pdo, grads, pc.scale, 25, bfl)
+        if batt["value"]:
+            batt["backward_over_reference"] = round(btf / batt["value"], 4)
+        result["prefill_backward"]["vendor_attention_reference"] = batt
 
     if args.calibration_copy:
         # one elementwise kernel that reads 256 MiB and writes 256 MiB, the

@@ -52,6 +52,9 @@ def test_default_bench_line():
     att = d["prefill"]["vendor_attention_reference"]
     if att["value"] is not None:   # the same attention within the bf16 tolerance
         assert att["max_abs_diff_from_this_library"] <= 2e-2
+    batt = d["prefill_backward"]["vendor_attention_reference"]
+    if batt["value"] is not None:   # the same gradients, relative to each one's largest magnitude
+        assert batt["max_rel_diff_from_this_library"] <= 2e-2
 
 
 def test_more_than_one_gpu_exits_with_a_message():
