@@ -236,6 +236,32 @@ def vendor_attention_backward_reference(torch, q, k, v, dout, ours, scale: float
             "max_rel_diff_from_this_library": round(rel, 6)}
 
 
+def vendor_decode_reference(torch, q, ks, vs, ours, scale: float, iters: int, kv_bytes: int) -> dict:
+    """torch's own attention for the same decode step: the one query token of
+    every head against the whole cache (every sequence full, so no mask),
+    flash backend forced, K/V read in place through enable_gqa, rotated over
+    the same cache copies and timed like the step.  Context for the decode
+    rate, with the largest difference from this library's output."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    name = "torch scaled_dot_product_attention, flash backend, enable_gqa, one query token"
+    q4 = q.unsqueeze(2)
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            def call(i):
+                return F.scaled_dot_product_attention(q4, ks[i % len(ks)], vs[i % len(vs)], scale=scale,
+                                                      enable_gqa=True)
+
+            o = call(0)
+            torch.cuda.synchronize()
+            diff = float((o.squeeze(2).float() - ours).abs().max())
+            ms = event_time_ms(call, iters, torch)
+    except RuntimeError as e:
+        return {"kernel": name, "value": None, "unit": "GB/s", "error": str(e)[:200]}
+    return {"kernel": name, "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(ms, 5), "max_abs_diff_from_this_library": round(diff, 6)}
+
+
 def record_counters(fetch_csv: str, write_csv: str, workload: str) -> dict:
     """Build profiles/counters.json from two rocprofv3 --pmc runs of
     ``bench.py --calibration-copy`` (one with FETCH_SIZE, one with WRITE_SIZE).
@@ -665,6 +691,12 @@ def main():
                      "ms_per_launch": round(ms_split, 5)},
         "timed_wall_s": round(wall, 4),
     }
+    if not (paged or fp8) and cfg.dtype == "bf16" and bool(np.all(inp.seq_lens == cfg.max_seq_len)):
+        step(0)   # out holds this library's result for the first cache copy
+        vref = vendor_decode_reference(torch, q, ks, vs, out, cfg.scale, max(20, args.steps // 2), kv_bytes)
+        if vref["value"]:
+            vref["step_over_reference"] = round(value / vref["value"], 4)
+        result["vendor_attention_reference"] = vref
 
     if args.expanded and cfg.dtype == "bf16" and not (paged or fp8) and Hq > Hkv:
         result["expanded_ab"] = expanded_ab(args, torch, gi, gqa, q, ks, vs, lens, out, cfg, inp, ms_step)
