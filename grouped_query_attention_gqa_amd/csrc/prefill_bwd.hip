@@ -137,16 +137,21 @@ void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // row_terms[0] = lse * log2(e), row_terms[1] = D, each [B, Hq, N]
   if (pos < n) row_terms[(size_t)j * rows + row_idx] = j == 0 ? lse2 : drow;
 
-  int a_rd[2][KSTEPS];           // K / V rows: key 32 kb + row, chunk 2 kk + j
-  int t_rd[4][DB], t_dx[4][DB];  // K^T: keys of 16-key chunk c, columns of block db
+  // LDS operand offsets.  The tile swizzle repeats every 16 rows, so key
+  // block kb (32 rows) and 16-key chunk c are the constant offsets 32 kb D
+  // and 16 c D from the offsets kept here.
+  int a_rd[KSTEPS];            // K / V rows: key row (of block 0), chunk 2 kk + j
+  int t_rd[DB], t_dx[DB];      // K^T: keys of 16-key chunk 0, columns of block db
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    a_rd[kk] = tiles::row_offset<D>(row, 2 * kk + j);
+    asm volatile("" : "+v"(a_rd[kk]));
+  }
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) a_rd[kb][kk] = tiles::row_offset<D>(32 * kb + row, 2 * kk + j);
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) tiles::tr_offsets<D>(lane, c, db, t_rd[c][db], t_dx[c][db]);
+  for (int db = 0; db < DB; ++db) {
+    tiles::tr_offsets<D>(lane, 0, db, t_rd[db], t_dx[db]);
+    asm volatile("" : "+v"(t_rd[db]));
+  }
 
   const size_t kv_off = ((size_t)b * hkv + kvh) * (size_t)n * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, n * D * 2);
@@ -161,31 +166,36 @@ void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave_hi = min(n, pos0 + 32);     // keys this wavefront needs
   const int ntiles = (min(n, q0 + mq) + kTile - 1) / kTile;
 
-  auto tile = [&](const __bf16* ks, const __bf16* vs, int t0) {
+  // dS of element r of block kb (P recomputed from lse) into its B-operand
+  // slot: element r of block kb is key t0 + 32 kb + 8 (r/4) + 4 j + r%4.
+  auto grad = [&](const f32x16 (&sc)[2], const f32x16 (&dp)[2], bf16x8 (&dsb)[4], int kb, int r) {
+    float ds = fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -lse2)) * (dp[kb][r] - drow);
+    asm volatile("" : "+v"(ds));   // keeps it in its group (not sunk to its use)
+    dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)ds;
+  };
+
+  // A tile that crosses the diagonal (or the end): the keys past each row
+  // get P = 0.  The products run one after the other.
+  auto tile_edge = [&](const __bf16* ks, const __bf16* vs, int t0) {
     // S^T and dP^T [64 keys, 32 rows] = K Q^T and V dO^T
     f32x16 sc[2] = {f32x16{}, f32x16{}};
     f32x16 dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(load_bf16x8(ks + a_rd[kb][kk]), qb[kk], sc[kb]);
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(load_bf16x8(ks + a_rd[kk] + 32 * kb * D), qb[kk], sc[kb]);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(load_bf16x8(vs + a_rd[kb][kk]), ob[kk], dp[kb]);
-    // dS^T in the B-operand order of the 16-key chunks: element r of block
-    // kb is key t0 + 32 kb + 8 (r/4) + 4 j + r%4.
-    const bool edge = t0 + kTile > pos0 || t0 + kTile > n;
+      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(load_bf16x8(vs + a_rd[kk] + 32 * kb * D), ob[kk], dp[kb]);
     bf16x8 dsb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(sc[kb][r], scale_log2, -lse2));
-        if (edge) {
-          const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
-          p = t <= lim ? p : 0.f;
-        }
+        const int t = t0 + 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
+        p = t <= lim ? p : 0.f;
         dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - drow));
       }
     // dQ^T [d, rows] += K^T [d, 16 keys] dS^T [16 keys, rows]
@@ -193,7 +203,58 @@ void prefill_bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc[db] = mfma32(tiles::read_tr<D>(ks, t_rd[c][db], t_dx[c][db]), dsb[c], acc[db]);
+        acc[db] = mfma32(tiles::read_tr<D>(ks + 16 * c * D, t_rd[db], t_dx[db]), dsb[c], acc[db]);
+  };
+
+  // A tile below the diagonal: the same arithmetic, with the dS of each key
+  // block computed between independent MFMAs of this wavefront, in groups
+  // fenced by scheduling barriers: dS of block 0 while the S^T and dP^T
+  // products of block 1 run, the first half of block 1's dS while the dQ^T
+  // products of block 0's dS run, and its second half beside those of the
+  // first half.  The products accumulate in the same order as in tile_edge.
+  auto tile_inner = [&](const __bf16* ks, const __bf16* vs) {
+    constexpr int kPerB = 8 / KSTEPS;   // dS elements per S^T / dP^T product of block 1
+    constexpr int kPerC = 4 / DB;       // ... per dQ^T product of chunks 0 and 1
+    constexpr int kPerD = 8 / DB;       // ... per dQ^T product of chunk 2
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) sc[0] = mfma32(load_bf16x8(ks + a_rd[kk]), qb[kk], sc[0]);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) dp[0] = mfma32(load_bf16x8(vs + a_rd[kk]), ob[kk], dp[0]);
+    bf16x8 dsb[4];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS; ++i) {   // S^T of block 1, then its dP^T
+      const int kk = i % KSTEPS;
+      if (i < KSTEPS)
+        sc[1] = mfma32(load_bf16x8(ks + a_rd[kk] + 32 * D), qb[kk], sc[1]);
+      else
+        dp[1] = mfma32(load_bf16x8(vs + a_rd[kk] + 32 * D), ob[kk], dp[1]);
+#pragma unroll
+      for (int r = i * kPerB; r < (i + 1) * kPerB; ++r) grad(sc, dp, dsb, 0, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {   // product i: key chunk i / DB, column block i % DB
+      acc[i % DB] = mfma32(tiles::read_tr<D>(ks + 16 * (i / DB) * D, t_rd[i % DB], t_dx[i % DB]), dsb[i / DB],
+                           acc[i % DB]);
+      if (i < 2 * DB) {
+#pragma unroll
+        for (int r = i * kPerC; r < (i + 1) * kPerC; ++r) grad(sc, dp, dsb, 1, r);
+      } else if (i < 3 * DB) {
+#pragma unroll
+        for (int r = 8 + (i - 2 * DB) * kPerD; r < 8 + (i - 2 * DB + 1) * kPerD; ++r) grad(sc, dp, dsb, 1, r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto tile = [&](const __bf16* ks, const __bf16* vs, int t0) {
+    if (t0 + kTile > pos0 || t0 + kTile > n)
+      tile_edge(ks, vs, t0);
+    else
+      tile_inner(ks, vs);
   };
 
   fill.issue2(k0s, rk, v0s, rv, w, 0);
