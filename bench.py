@@ -577,9 +577,18 @@ def main():
         sys.exit(2)
     gqa.load_library()   # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    cus, khz = gqa.gqa_device_info(0)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": cus,
+              "max_clock_mhz": round(khz / 1000.0, 1),
+              # gfx950 matrix cores: 4,096 dense bf16 FLOP per clock per compute unit
+              "bf16_dense_peak_tflops_from_props": round(cus * 4096 * khz * 1e3 / 1e12, 1),
+              "note": "the roofline peaks are the published 8 TB/s and 2.5 PFLOP/s"}
 
     if args.workload == "mla-decode":
-        print(json.dumps(bench_wide(args, torch, gi, gqa)), flush=True)
+        res = bench_wide(args, torch, gi, gqa)
+        res["device"] = device
+        print(json.dumps(res), flush=True)
         return
 
     paged = args.workload.startswith("paged-")
@@ -791,6 +800,7 @@ def main():
         if "prefill" in result:
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(p, args.cpu_budget)
     result["context_from_pages"] = PAGE_FIGURES
+    result["device"] = device
 
     print(json.dumps(result), flush=True)
 

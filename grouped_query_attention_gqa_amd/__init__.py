@@ -23,7 +23,7 @@ from typing import NamedTuple, Optional
 import torch
 
 __all__ = [
-    "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version",
+    "GqaError", "Plan", "load_library", "library_path", "gqa_abi_version", "gqa_device_info",
     "gqa_decode_plan", "gqa_decode_workspace_bytes", "decode_workspace", "gqa_decode", "gqa_decode_noalloc", "gqa_decode_split",
     "gqa_decode_merge",
     "gqa_prefill_causal", "gqa_prefill_backward_workspace", "gqa_prefill_causal_backward",
@@ -76,6 +76,8 @@ def load_library():
     lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_decode_workspace_bytes.argtypes = [I32] * 4
     lib.gqa_last_hip_error.restype = ctypes.c_char_p
+    lib.gqa_device_info.restype = I32
+    lib.gqa_device_info.argtypes = [I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.gqa_decode_plan.restype = I32
     lib.gqa_decode_plan.argtypes = [I32] * 7 + [ctypes.POINTER(I32), ctypes.POINTER(I32),
                                                 ctypes.POINTER(I64)]
@@ -112,6 +114,13 @@ def load_library():
 
 def gqa_abi_version() -> int:
     return load_library().gqa_abi_version()
+
+
+def gqa_device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) of a HIP device."""
+    cus, khz = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("gqa_device_info", load_library().gqa_device_info(device, ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
 
 
 def _check(fn: str, status: int):

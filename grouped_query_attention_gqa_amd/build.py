@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "decode.hip", "decode_wide.hip", "prefill.hip", "prefill_bwd.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_wide.hip", "device_info.hip", "prefill.hip", "prefill_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -77,6 +77,15 @@ const char* gqa_status_str(gqa_status status);
 /* Text of the last HIP error seen by a call on this thread ("" if none). */
 const char* gqa_last_hip_error(void);
 
+/* Compute units and peak shader clock (kHz) of HIP device `device`, as
+ * hipDeviceGetAttribute reports them, for deriving the roofline peaks of the
+ * board a measurement runs on (the dense bf16 matrix-core rate is compute
+ * units x 4,096 FLOP per clock on gfx950).  Host-side query, synchronous; no
+ * kernel runs.  Errors: a null output pointer -> GQA_ERR_NULL (checked before
+ * any HIP call), a failed query -> GQA_ERR_HIP (outputs left unchanged; this
+ * call does not record the HIP error's text for gqa_last_hip_error). */
+int32_t gqa_device_info(int32_t device, int32_t* compute_units, int32_t* max_clock_khz);
+
 /*
  * Launch plan of a decode call.  Decode lays the cached tokens of every
  * (sequence, KV head, block of up to 16 query heads; for bf16 and E4M3

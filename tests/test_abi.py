@@ -45,6 +45,7 @@ BOUNDARY_CALLS = {"gqa_decode", "gqa_decode_workspace_bytes", "gqa_prefill_causa
 EXTRA_CALLS = {
     "gqa_status_string": "status text taking the int32 the calls return (gqa_status_str takes the enum)",
     "gqa_last_hip_error": "text of the HIP error behind GQA_ERR_HIP",
+    "gqa_device_info": "compute units and clock of the device, to derive the roofline peaks of the board measured",
     "gqa_decode_plan": "exact workspace for one (Hkv, dtype, range size), the grid and the range size",
     "gqa_decode_noalloc": "gqa_decode for callers that cannot allocate (library-owned per-GPU scratch)",
     "gqa_decode_split": "first decode stage alone (partials), the cut a sequence-parallel decode merges across",
@@ -97,6 +98,13 @@ def test_version_and_status_strings(lib):
         assert lib.gqa_status_string(code) == name
     assert lib.gqa_status_string(99) == b"GQA_ERR_UNKNOWN"
     assert lib.gqa_last_hip_error() == b""
+
+
+def test_device_info_rejects_null_outputs(lib):
+    x = ctypes.c_int32(7)
+    assert lib.gqa_device_info(0, None, ctypes.byref(x)) == NULL
+    assert lib.gqa_device_info(0, ctypes.byref(x), None) == NULL
+    assert x.value == 7   # checked before any HIP call; nothing written
 
 
 def test_plan_auto_and_explicit():

@@ -41,6 +41,8 @@ def test_default_bench_line():
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], abs=1e-4)
     # the step (split + merge) reads the same K/V as the split kernel alone, so it is not faster
     assert d["value"] <= rf["achieved"] * 1.05
+    dev = d["device"]
+    assert dev["compute_units"] > 0 and dev["max_clock_mhz"] > 0 and dev["bf16_dense_peak_tflops_from_props"] > 0
     vref = d["vendor_attention_reference"]
     if vref["value"] is not None:   # the same attention within the bf16 tolerance
         assert vref["max_abs_diff_from_this_library"] <= 2e-2
